@@ -1,0 +1,307 @@
+"""Seeded synthetic operands for tree-verification attention.
+
+This module draws the operands of one attention layer of a speculative-decoding verify step:
+prefix lengths, a topologically ordered draft-tree parent array, and Q / K / V values. It holds
+none of the attention arithmetic. Both the HIP path and the CPU oracle receive exactly the arrays
+built here: bf16 values travel as raw uint16 bit patterns, fp32 values as float32.
+
+Shapes follow the operands of LongSpec's Hybrid Tree Attention (LongSpec page, "Fast tree
+attention" section): Q for the tree nodes, a committed K/V prefix that needs no mask, and the
+speculative (tree) K/V. Tree nodes are numbered in topological order (DFlash-TfM summary page,
+"Rollback-free tree verification"): parent[i] is in [-1, i-1], and -1 means the node hangs
+directly off the committed prefix.
+
+Draw order for one seed (numpy PCG64): prefix lengths -> parent arrays -> outlier channels ->
+Q -> K prefix -> V prefix -> K tree -> V tree. Values are fp32 N(0, 1), rounded to bf16 with
+round-to-nearest-even. Padding rows beyond a sequence's length are not drawn; they are filled
+with NaN ("nan", used by tests to catch out-of-range reads) or zeros ("finite", used for timing).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic layer shape. ``L`` is a fixed prefix length or an inclusive (lo, hi) range."""
+
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    T: int
+    L: object
+    dtype: str = "bf16"          # "bf16" or "f32"
+    tree: str = "bounded"        # "uniform", "bounded", "chain", "star", "single", "beam"
+    depth_cap: int = 8
+    branch_cap: int = 4
+    outlier_channels: int = 0
+    outlier_scale: float = 8.0
+    widths: tuple = ()
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The long-context shapes measured on the pages' target families (LongSpec page, experiments),
+# sized for one layer. Sweep entries differ only in tree size and shape.
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", B=1, Hq=4, Hkv=1, D=64, T=8, L=256, dtype="f32",
+                         tree="uniform"),
+    "mha_7b": Workload("mha_7b", B=1, Hq=32, Hkv=32, D=128, T=64, L=16384),
+    "gqa_64k": Workload("gqa_64k", B=4, Hq=32, Hkv=8, D=128, T=64, L=(32768, 65536)),
+    "gqa_64k_pinned": Workload("gqa_64k_pinned", B=4, Hq=32, Hkv=8, D=128, T=64, L=65536),
+    "sweep_t1": Workload("sweep_t1", B=8, Hq=32, Hkv=8, D=128, T=1, L=32768, tree="single"),
+    "sweep_t6": Workload("sweep_t6", B=8, Hq=32, Hkv=8, D=128, T=6, L=32768, tree="chain"),
+    "sweep_t16": Workload("sweep_t16", B=8, Hq=32, Hkv=8, D=128, T=16, L=32768),
+    "sweep_t32": Workload("sweep_t32", B=8, Hq=32, Hkv=8, D=128, T=32, L=32768),
+    "sweep_t64": Workload("sweep_t64", B=8, Hq=32, Hkv=8, D=128, T=64, L=32768),
+    "sweep_t128": Workload("sweep_t128", B=8, Hq=32, Hkv=8, D=128, T=128, L=32768),
+    "long_reasoning": Workload("long_reasoning", B=1, Hq=40, Hkv=8, D=128, T=128, L=131072,
+                               depth_cap=12, outlier_channels=4),
+    # Beam-search-shaped tree (LongSpec page, experimental details: beam widths per step),
+    # cut to a 64-node budget.
+    "gqa_64k_beam": Workload("gqa_64k_beam", B=4, Hq=32, Hkv=8, D=128, T=64, L=65536,
+                             tree="beam", widths=(4, 16, 16, 16, 12)),
+}
+
+
+@dataclasses.dataclass
+class Case:
+    """Operands of one layer. All arrays are host numpy arrays in C order."""
+
+    wl: Workload
+    seed: int
+    seq_lens: np.ndarray            # int32 [B]
+    parent: np.ndarray              # int32 [B, T]
+    q: np.ndarray                   # [B, T, Hq, D]
+    k_cache: np.ndarray             # contiguous [B, Lcap, Hkv, D] or paged pool [P, page, Hkv, D]
+    v_cache: np.ndarray
+    k_tree: np.ndarray              # [B, T, Hkv, D]
+    v_tree: np.ndarray
+    block_table: Optional[np.ndarray] = None   # int32 [B, max_blocks] when paged
+    page_size: int = 0
+    lcap: int = 0                   # rows per sequence (contiguous) or max_blocks * page_size
+    outlier_channels: Optional[np.ndarray] = None
+
+    @property
+    def paged(self) -> bool:
+        return self.block_table is not None
+
+    @property
+    def dtype(self) -> str:
+        return self.wl.dtype
+
+    @property
+    def scale(self) -> float:
+        return self.wl.scale
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (round to nearest, ties to even); returns the uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ---------------------------------------------------------------------------------------------
+# trees
+
+
+def uniform_tree(rng: np.random.Generator, T: int) -> np.ndarray:
+    """parent[i] drawn uniformly from [-1, i-1]."""
+    return np.array([rng.integers(-1, i) for i in range(T)], dtype=np.int32)
+
+
+def bounded_tree(rng: np.random.Generator, T: int, depth_cap: int, branch_cap: int) -> np.ndarray:
+    """Random tree with node depth <= depth_cap and at most branch_cap children per node.
+
+    Node i picks its parent uniformly among the eligible ones: the prefix (-1) while it has fewer
+    than branch_cap children, and every earlier node j whose depth is below depth_cap and that
+    has fewer than branch_cap children. Root-attached nodes have depth 1.
+    """
+    parent = np.empty(T, dtype=np.int32)
+    depth = np.zeros(T, dtype=np.int64)
+    children = np.zeros(T, dtype=np.int64)
+    root_children = 0
+    for i in range(T):
+        elig = [-1] if root_children < branch_cap else []
+        elig += [j for j in range(i) if depth[j] < depth_cap and children[j] < branch_cap]
+        p = elig[int(rng.integers(len(elig)))]
+        parent[i] = p
+        if p < 0:
+            root_children += 1
+            depth[i] = 1
+        else:
+            children[p] += 1
+            depth[i] = depth[p] + 1
+    return parent
+
+
+def beam_tree(rng: np.random.Generator, widths, branch_cap: int) -> np.ndarray:
+    """Layered tree: layer k has widths[k] nodes whose parents come from layer k-1."""
+    parent = []
+    prev = [-1]
+    for w in widths:
+        kids = {p: 0 for p in prev}
+        layer = []
+        for _ in range(w):
+            elig = [p for p in prev if p < 0 or kids[p] < branch_cap]
+            p = elig[int(rng.integers(len(elig)))]
+            kids[p] += 1
+            layer.append(len(parent))
+            parent.append(p)
+        prev = layer
+    return np.array(parent, dtype=np.int32)
+
+
+def make_tree(rng: np.random.Generator, wl: Workload) -> np.ndarray:
+    T = wl.T
+    if wl.tree == "uniform":
+        return uniform_tree(rng, T)
+    if wl.tree == "bounded":
+        return bounded_tree(rng, T, wl.depth_cap, wl.branch_cap)
+    if wl.tree == "chain":
+        return np.arange(-1, T - 1, dtype=np.int32)
+    if wl.tree in ("star", "single"):
+        return np.full(T, -1, dtype=np.int32)
+    if wl.tree == "beam":
+        par = beam_tree(rng, wl.widths, wl.branch_cap)
+        assert len(par) == T, (len(par), T)
+        return par
+    raise ValueError(f"unknown tree kind {wl.tree!r}")
+
+
+# ---------------------------------------------------------------------------------------------
+# cases
+
+
+def _draw_values(rng, shape, dtype, scale_channels=None, scale=1.0, chunk_rows=1 << 14):
+    """Draw N(0,1) fp32 values of ``shape`` (leading axis chunked) and convert to ``dtype``.
+
+    ``scale_channels`` multiplies the listed last-axis channels by ``scale`` before rounding.
+    """
+    out_dtype = np.uint16 if dtype == "bf16" else np.float32
+    out = np.empty(shape, dtype=out_dtype)
+    n = shape[0]
+    for s in range(0, max(n, 1), chunk_rows):
+        e = min(n, s + chunk_rows)
+        if e <= s:
+            break
+        x = rng.standard_normal((e - s,) + tuple(shape[1:]), dtype=np.float32)
+        if scale_channels is not None and len(scale_channels):
+            x[..., scale_channels] *= np.float32(scale)
+        out[s:e] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    return out
+
+
+def _pad_value(dtype, pad):
+    if pad == "nan":
+        return BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+    return np.uint16(0) if dtype == "bf16" else np.float32(0.0)
+
+
+def make_case(wl: Workload, seed: int = 0, *, layout: str = "contiguous", pad: str = "nan",
+              page_size: int = 64, lens=None, parent=None, lcap: Optional[int] = None) -> Case:
+    """Build the operands of ``wl`` for ``seed``.
+
+    ``lens`` / ``parent`` override the drawn prefix lengths / parent arrays (the draws still
+    happen, so the value streams do not shift). ``layout`` is "contiguous" or "paged"; the paged
+    pool places each page at a seeded random physical slot, and unused block-table entries point
+    at a page filled with the pad value.
+    """
+    if layout not in ("contiguous", "paged"):
+        raise ValueError(layout)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, T, Hq, Hkv, D = wl.B, wl.T, wl.Hq, wl.Hkv, wl.D
+    if isinstance(wl.L, tuple):
+        drawn = rng.integers(wl.L[0], wl.L[1], size=B, endpoint=True).astype(np.int32)
+    else:
+        drawn = np.full(B, int(wl.L), dtype=np.int32)
+    seq_lens = drawn if lens is None else np.asarray(lens, dtype=np.int32).reshape(B)
+    drawn_par = np.stack([make_tree(rng, wl) for _ in range(B)]) if T else np.zeros((B, 0), np.int32)
+    par = drawn_par if parent is None else np.asarray(parent, dtype=np.int32).reshape(B, T)
+    chans = None
+    if wl.outlier_channels:
+        chans = np.sort(rng.choice(D, wl.outlier_channels, replace=False)).astype(np.int64)
+
+    dt = wl.dtype
+    q = _draw_values(rng, (B * T, Hq, D), dt).reshape(B, T, Hq, D)
+    padv = _pad_value(dt, pad)
+    maxlen = int(seq_lens.max()) if B else 0
+    if layout == "contiguous":
+        cap = maxlen if lcap is None else int(lcap)
+        if cap < maxlen:
+            raise ValueError("lcap below the longest prefix")
+        kc = np.full((B, cap, Hkv, D), padv)
+        vc = np.full((B, cap, Hkv, D), padv)
+        for b in range(B):
+            kc[b, :seq_lens[b]] = _draw_values(rng, (int(seq_lens[b]), Hkv, D), dt, chans,
+                                               wl.outlier_scale)
+        for b in range(B):
+            vc[b, :seq_lens[b]] = _draw_values(rng, (int(seq_lens[b]), Hkv, D), dt)
+        block_table = None
+        psz = 0
+    else:
+        psz = int(page_size)
+        if psz < 16 or psz & (psz - 1):
+            raise ValueError("page_size must be a power of two >= 16")
+        npg = [(int(n) + psz - 1) // psz for n in seq_lens]
+        max_blocks = max(max(npg) if npg else 0, 1)
+        if lcap is not None:
+            max_blocks = max(max_blocks, (int(lcap) + psz - 1) // psz)
+        cap = max_blocks * psz
+        n_pages = sum(npg) + 1                      # the last physical page is the pad page
+        perm = np.random.Generator(np.random.PCG64([seed, 1])).permutation(n_pages - 1)
+        pad_page = n_pages - 1
+        kc = np.full((n_pages, psz, Hkv, D), padv)
+        vc = np.full((n_pages, psz, Hkv, D), padv)
+        block_table = np.full((B, max_blocks), pad_page, dtype=np.int32)
+        nxt = 0
+        for b in range(B):
+            for blk in range(npg[b]):
+                block_table[b, blk] = perm[nxt]
+                nxt += 1
+
+        def scatter(dst, b, vals):
+            n = int(seq_lens[b])
+            for blk in range(npg[b]):
+                rows = vals[blk * psz:min(n, (blk + 1) * psz)]
+                dst[block_table[b, blk], :len(rows)] = rows
+
+        for b in range(B):
+            scatter(kc, b, _draw_values(rng, (int(seq_lens[b]), Hkv, D), dt, chans,
+                                        wl.outlier_scale))
+        for b in range(B):
+            scatter(vc, b, _draw_values(rng, (int(seq_lens[b]), Hkv, D), dt))
+    kt = _draw_values(rng, (B * T, Hkv, D), dt, chans, wl.outlier_scale).reshape(B, T, Hkv, D)
+    vt = _draw_values(rng, (B * T, Hkv, D), dt).reshape(B, T, Hkv, D)
+    return Case(wl=wl, seed=seed, seq_lens=seq_lens, parent=par, q=q, k_cache=kc, v_cache=vc,
+                k_tree=kt, v_tree=vt, block_table=block_table, page_size=psz, lcap=cap,
+                outlier_channels=chans)
+
+
+def tree_depths(parent: np.ndarray) -> np.ndarray:
+    """Depth of every node of one parent array (root-attached nodes have depth 1)."""
+    d = np.zeros(len(parent), dtype=np.int64)
+    for i, p in enumerate(parent):
+        d[i] = 1 if p < 0 else d[p] + 1
+    return d
