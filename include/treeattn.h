@@ -1,0 +1,176 @@
+/*
+ * treeattn.h -- C ABI of the MI355X (gfx950) tree-verification attention library.
+ *
+ * The operation is LongSpec's Hybrid Tree Attention (LongSpec page, "Fast tree attention"
+ * section): every node of a draft tree attends to the committed KV prefix with no mask and to
+ * the tree's own keys under an ancestor mask, and the two partial results are merged through
+ * their log-sum-exps (same section, aggregation equations; appendix "Correctness of attention
+ * aggregation", Proposition). The library computes, for tree node i of sequence b and query
+ * head h,
+ *
+ *     O[b,i,h]   = sum_j softmax_j(s_j) * v_j,      LSE[b,i,h] = ln sum_j exp(s_j),
+ *     s_j        = scale * q[b,i,h] . k_j,
+ *
+ * with j running over the prefix keys 0..seq_lens[b]-1 and over the tree nodes that are i or
+ * an ancestor of i. Query head h reads KV head h / (Hq / Hkv).
+ *
+ * Conventions shared by every call:
+ *   - Pointers are device pointers unless stated otherwise. The caller allocates and owns all
+ *     memory, including the workspace; the library allocates nothing, keeps no pointer after a
+ *     call returns and holds no mutable global state.
+ *   - All work is enqueued on ``stream`` (0 = the null stream); no call synchronises the host.
+ *   - Return values are ta_status codes. Argument errors are reported before anything is
+ *     enqueued. Errors that only the device can see (a parent index out of range, a prefix
+ *     length above the KV capacity, a block-table entry outside the page pool) are reported by
+ *     writing a nonzero TA_DEV_* bit into ``*err_flag`` (atomic OR; pass NULL to skip). The
+ *     caller clears the flag and reads it after synchronising. Out-of-range parents are treated
+ *     as -1 and lengths are clamped, so no invalid address is ever read.
+ *   - Strides are in elements. The innermost (head_dim) stride is 1 for every tensor, and every
+ *     row base must be 16-byte aligned.
+ */
+#ifndef TREEATTN_H
+#define TREEATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ta_status {
+    TA_OK = 0,
+    TA_EINVAL = 1,        /* null pointer, bad shape, stride or alignment, Hq % Hkv != 0, T > 256 */
+    TA_EUNSUPPORTED = 2,  /* head_dim not in {64, 128}, unknown dtype */
+    TA_EWORKSPACE = 3,    /* workspace missing or smaller than tree_attn_workspace_size() */
+    TA_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} ta_status;
+
+typedef enum ta_dtype {
+    TA_BF16 = 0,          /* bfloat16 inputs; fp32 accumulation */
+    TA_F32 = 1            /* float32 inputs and arithmetic */
+} ta_dtype;
+
+/* Bits written into *err_flag by the device. */
+#define TA_DEV_BAD_PARENT 1u   /* parent[b][i] outside [-1, i-1] */
+#define TA_DEV_BAD_LEN 2u      /* seq_lens[b] outside [0, capacity] */
+#define TA_DEV_BAD_PAGE 4u     /* a block-table entry used by a prefix outside [0, num_pages) */
+
+/* Largest tree the kernels accept. */
+#define TA_MAX_TREE 256
+
+/*
+ * One attention layer of a verify step. Plain C struct, read during the call only.
+ *
+ * Operands (the pages' statement of the problem: Q for the tree nodes, the cache part
+ * {K_cache, V_cache} and the speculative part {K_specs, V_specs}, plus the tree):
+ *   q          [B, T, Hq, D] with strides (q_sb, q_st, q_sh); dtype ``dtype``.
+ *   k_cache,   committed prefix. Contiguous layout (block_table == NULL): [B, Lmax, Hkv, D]
+ *   v_cache    with strides (kv_s0 = batch, kv_s1 = row, kv_s2 = head). Paged layout: a page
+ *              pool [num_pages, page_size, Hkv, D] with strides (kv_s0 = page, kv_s1 = row,
+ *              kv_s2 = head); key j of sequence b lives in page block_table[b][j / page_size]
+ *              at row j % page_size. K and V share one stride set.
+ *   seq_lens   int32 [B]: prefix length of each sequence, 0 <= seq_lens[b] <= capacity, where
+ *              capacity = Lmax (contiguous) or max_blocks * page_size (paged).
+ *   block_table int32 [B, max_blocks] or NULL. page_size is a power of two >= 16.
+ *   k_tree,    the T tree nodes' keys and values, [B, T, Hkv, D] with strides
+ *   v_tree     (kt_sb, kt_st, kt_sh), shared by K and V.
+ *   parent     int32 [B, T], topological: parent[b][i] in [-1, i-1]; -1 hangs node i directly
+ *              off the committed prefix (DFlash-TfM summary page, "Rollback-free tree
+ *              verification": the tree is sorted topologically).
+ *   scale      the logit scale, normally 1/sqrt(D).
+ *   num_splits number of KV splits of the prefix, or 0 to let the library choose.
+ */
+typedef struct ta_problem {
+    int32_t B, T, Hq, Hkv, D;
+    int32_t dtype;
+    float scale;
+    int32_t num_splits;
+    const void *q;
+    int64_t q_sb, q_st, q_sh;
+    const void *k_cache;
+    const void *v_cache;
+    int64_t kv_s0, kv_s1, kv_s2;
+    const int32_t *seq_lens;
+    const int32_t *block_table;
+    int32_t Lmax, page_size, max_blocks, num_pages;
+    const void *k_tree;
+    const void *v_tree;
+    int64_t kt_sb, kt_st, kt_sh;
+    const int32_t *parent;
+} ta_problem;
+
+/*
+ * Ancestor-or-self mask of a batch of draft trees (LongSpec page, "Fast tree attention": the
+ * tree mask disables attention between speculative tokens of different branches; textbook page,
+ * "Linear chains and candidate trees consume work differently": each node only attends to its
+ * ancestors). parent: int32 [B, T], 1 <= T <= 256. mask: uint64 [B, T, W], W = ceil(T / 64);
+ * bit (j % 64) of word j / 64 of row i is set exactly when j == i or j is an ancestor of i.
+ * Invalid parents set TA_DEV_BAD_PARENT and are treated as -1.
+ */
+int tree_mask_build(const int32_t *parent, int B, int T, uint64_t *mask, int32_t *err_flag,
+                    hipStream_t stream);
+
+/*
+ * Host-only. Bytes of workspace that tree_attn_prefix and tree_attn_forward need for ``p``
+ * (the per-split partial outputs and log-sum-exps, fp32). Writes *bytes; returns TA_EINVAL /
+ * TA_EUNSUPPORTED for a problem the other calls would reject.
+ */
+int tree_attn_workspace_size(const ta_problem *p, size_t *bytes);
+
+/* Host-only. The number of prefix splits the library uses for ``p`` (after automatic choice). */
+int tree_attn_num_splits(const ta_problem *p, int *num_splits);
+
+/*
+ * Unmasked attention of every tree query over its sequence's committed prefix -- the cache part
+ * of the divide-and-aggregate step (LongSpec page, "Fast tree attention", splitting the
+ * key-value pairs). o_c: fp32 [B, T, Hq, D]; lse_c: fp32 [B, T, Hq] (natural log). A sequence
+ * with an empty prefix gets O = 0 and LSE = -inf. ``ws`` is device memory of at least
+ * tree_attn_workspace_size() bytes, 256-byte aligned.
+ */
+int tree_attn_prefix(const ta_problem *p, float *o_c, float *lse_c, void *ws, size_t ws_bytes,
+                     int32_t *err_flag, hipStream_t stream);
+
+/*
+ * Masked attention of every tree query over the tree's own keys -- the speculative part
+ * (same section). Node i sees node j iff j == i or j is an ancestor of i; the mask is derived
+ * on the device from ``parent``. o_s: fp32 [B, T, Hq, D]; lse_s: fp32 [B, T, Hq]. Needs no
+ * workspace. Prefix fields of ``p`` are ignored.
+ */
+int tree_attn_tree(const ta_problem *p, float *o_s, float *lse_s, int32_t *err_flag,
+                   hipStream_t stream);
+
+/*
+ * Log-sum-exp aggregation of two partial results over disjoint key sets (LongSpec page, "Fast
+ * tree attention", aggregation equations; appendix Proposition):
+ *     LSE = ln(exp(LSE_a) + exp(LSE_b)),  O = O_a exp(LSE_a - LSE) + O_b exp(LSE_b - LSE).
+ * Rows = B * T * Hq, each D wide, contiguous. o_a, o_b: fp32 [rows, D]; lse_a, lse_b: fp32
+ * [rows]; o: [rows, D] of o_dtype (TA_BF16 rounds to nearest even, or TA_F32); lse: fp32
+ * [rows]. Two empty parts (both -inf) give O = 0, LSE = -inf. Outputs may alias inputs of the
+ * same type only if they are identical pointers.
+ */
+int tree_attn_merge(int B, int T, int Hq, int D, const float *o_a, const float *lse_a,
+                    const float *o_b, const float *lse_b, void *o, int o_dtype, float *lse,
+                    hipStream_t stream);
+
+/*
+ * The whole hybrid tree attention of one layer: prefix (split over the KV length), masked tree
+ * part with the mask derived in-kernel, and the log-sum-exp aggregation of all partials, in two
+ * launches. o: [B, T, Hq, D] contiguous, of p->dtype; lse: fp32 [B, T, Hq] (natural log).
+ */
+int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t ws_bytes,
+                      int32_t *err_flag, hipStream_t stream);
+
+/* Static description of a status code. Never NULL. */
+const char *tree_attn_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int tree_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEATTN_H */

@@ -1,0 +1,135 @@
+"""C-ABI library checks that need no GPU: exports, status strings, argument validation.
+
+Nothing here enqueues GPU work: every call below is rejected (or answered) on the host before
+any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "treeattn.h")
+
+from tree_verification_attention_amd import _lib  # noqa: E402
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libtreeattn.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_every_declared_function_is_exported(lib):
+    declared = header_functions()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.tree_attn_abi_version() == 100
+    for code in range(5):
+        assert _lib.status_string(code)
+    assert _lib.status_string(99) == "unknown status"
+
+
+def problem(**kw):
+    p = _lib.TaProblem()
+    p.B, p.T, p.Hq, p.Hkv, p.D = 2, 8, 8, 2, 128
+    p.dtype = _lib.TA_BF16
+    p.scale = 128 ** -0.5
+    fake = 1 << 20  # a 16-byte aligned non-null placeholder; never dereferenced on the host
+    p.q = p.k_cache = p.v_cache = p.k_tree = p.v_tree = fake
+    p.seq_lens = p.parent = fake
+    p.q_sb, p.q_st, p.q_sh = 8 * 8 * 128, 8 * 128, 128
+    p.kv_s0, p.kv_s1, p.kv_s2 = 1000 * 2 * 128, 2 * 128, 128
+    p.kt_sb, p.kt_st, p.kt_sh = 8 * 2 * 128, 2 * 128, 128
+    p.Lmax = 1000
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def ws_size(lib, p):
+    n = ctypes.c_size_t(0)
+    rc = lib.tree_attn_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_is_host_only_and_sane(lib):
+    rc, n = ws_size(lib, problem())
+    assert rc == _lib.TA_OK
+    k = ctypes.c_int(0)
+    assert lib.tree_attn_num_splits(ctypes.byref(problem()), ctypes.byref(k)) == 0
+    rows = 2 * 8 * 8
+    assert n >= (k.value + 1) * rows * (128 + 1) * 4
+    # forced split count
+    k2 = ctypes.c_int(0)
+    assert lib.tree_attn_num_splits(ctypes.byref(problem(num_splits=3)), ctypes.byref(k2)) == 0
+    assert k2.value == 3
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("D", 96, _lib.TA_EUNSUPPORTED), ("dtype", 7, _lib.TA_EUNSUPPORTED),
+    ("T", 0, _lib.TA_EINVAL), ("T", 257, _lib.TA_EINVAL), ("Hq", 7, _lib.TA_EINVAL),
+    ("scale", 0.0, _lib.TA_EINVAL), ("scale", float("nan"), _lib.TA_EINVAL),
+    ("q", 0, _lib.TA_EINVAL), ("q", (1 << 20) + 8, _lib.TA_EINVAL),
+    ("q_st", 1001, _lib.TA_EINVAL), ("num_splits", -1, _lib.TA_EINVAL),
+])
+def test_invalid_problems_are_rejected_before_launch(lib, field, value, status):
+    p = problem(**{field: value})
+    rc, _ = ws_size(lib, p)
+    assert rc == status
+    o = ctypes.c_void_p(1 << 20)
+    assert lib.tree_attn_forward(ctypes.byref(p), o, o, o, 1 << 30, None, None) == status
+
+
+def test_forward_argument_errors(lib):
+    o = ctypes.c_void_p(1 << 20)
+    rc, need = ws_size(lib, problem())
+    for bad in (dict(seq_lens=0), dict(k_cache=0), dict(parent=0), dict(v_tree=0),
+                dict(kv_s1=100), dict(block_table=1 << 20, page_size=24, max_blocks=4,
+                                       num_pages=4),
+                dict(block_table=1 << 20, page_size=64, max_blocks=0, num_pages=4)):
+        assert lib.tree_attn_forward(ctypes.byref(problem(**bad)), o, o, o, need, None,
+                                     None) == _lib.TA_EINVAL, bad
+    # workspace checks
+    assert lib.tree_attn_forward(ctypes.byref(problem()), o, o, o, need - 1, None,
+                                 None) == _lib.TA_EWORKSPACE
+    assert lib.tree_attn_forward(ctypes.byref(problem()), o, o, None, need, None,
+                                 None) == _lib.TA_EWORKSPACE
+    assert lib.tree_attn_forward(ctypes.byref(problem()), o, o, ctypes.c_void_p((1 << 20) + 16),
+                                 need, None, None) == _lib.TA_EWORKSPACE
+    assert lib.tree_attn_prefix(ctypes.byref(problem()), o, None, o, need, None,
+                                None) == _lib.TA_EINVAL
+
+
+def test_merge_and_mask_argument_errors(lib):
+    o = ctypes.c_void_p(1 << 20)
+    assert lib.tree_attn_merge(1, 2, 3, 96, o, o, o, o, o, 0, o, None) == _lib.TA_EUNSUPPORTED
+    assert lib.tree_attn_merge(1, 2, 3, 64, o, o, o, o, o, 5, o, None) == _lib.TA_EUNSUPPORTED
+    assert lib.tree_attn_merge(1, 2, 3, 64, None, o, o, o, o, 0, o, None) == _lib.TA_EINVAL
+    assert lib.tree_attn_merge(0, 2, 3, 64, None, None, None, None, None, 0, None, None) == 0
+    assert lib.tree_mask_build(o, 1, 0, o, None, None) == _lib.TA_EINVAL
+    assert lib.tree_mask_build(o, 1, 257, o, None, None) == _lib.TA_EINVAL
+    assert lib.tree_mask_build(None, 1, 8, o, None, None) == _lib.TA_EINVAL
+    assert lib.tree_mask_build(None, 0, 8, None, None, None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        _lib.forward(q, q, q, torch.zeros(1, dtype=torch.int32), q[:, :, :1], q[:, :, :1],
+                     torch.zeros(1, 2, dtype=torch.int32))

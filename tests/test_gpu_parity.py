@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars: ancestor masks bit-exact; bf16 inputs max |dO| <= 2e-2 and max |dLSE| <= 1e-3; fp32
+inputs max |dO| <= 1e-4 and max |dLSE| <= 1e-4 (fp32 accumulation over at most a few thousand
+terms per lane, errors ~1e-6). Inputs are the generator's seeded cases; padding rows are NaN so
+that any read past a sequence's length shows up as a NaN in the output.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tree_verification_attention_amd import _lib, inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 1e-3), "f32": (1e-4, 1e-4)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a, dtype=None):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_gpu(case):
+    return dict(q=dev(case.q), k_cache=dev(case.k_cache), v_cache=dev(case.v_cache),
+                seq_lens=dev(case.seq_lens), k_tree=dev(case.k_tree), v_tree=dev(case.v_tree),
+                parent=dev(case.parent), block_table=dev(case.block_table),
+                page_size=case.page_size or None)
+
+
+def run_forward(case, **kw):
+    g = to_gpu(case)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, lse = _lib.forward(g["q"], g["k_cache"], g["v_cache"], g["seq_lens"], g["k_tree"],
+                            g["v_tree"], g["parent"], block_table=g["block_table"],
+                            page_size=g["page_size"], scale=case.scale, err=err, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy(), int(err.item())
+
+
+def check(case, o_gpu, lse_gpu, o_ref, lse_ref, what):
+    atol_o, atol_l = TOL[case.dtype]
+    o_gpu = o_gpu.reshape(o_ref.shape)
+    lse_gpu = lse_gpu.reshape(lse_ref.shape)
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse_gpu), fin), f"{what}: -inf pattern differs"
+    do = np.abs(o_gpu - o_ref).max() if o_ref.size else 0.0
+    dl = np.abs(lse_gpu[fin] - lse_ref[fin]).max() if fin.any() else 0.0
+    say(f"{what}: max|dO|={do:.3e} max|dLSE|={dl:.3e}")
+    assert do <= atol_o, f"{what}: max|dO| {do} > {atol_o}"
+    assert dl <= atol_l, f"{what}: max|dLSE| {dl} > {atol_l}"
+
+
+def wl(name="p", B=2, Hq=8, Hkv=2, D=128, T=16, L=(1, 700), dtype="bf16", tree="bounded", **kw):
+    return inputs.Workload(name, B=B, Hq=Hq, Hkv=Hkv, D=D, T=T, L=L, dtype=dtype, tree=tree, **kw)
+
+
+# ------------------------------------------------------------------------------------------------
+# mask
+
+
+def mask_gpu(parent):
+    m = _lib.mask_build(dev(parent))
+    torch.cuda.synchronize()
+    return m.cpu().numpy().view(np.uint64)
+
+
+def test_mask_example_chain_star():
+    par = np.array([[-1, 0, -1, 2, 2]], dtype=np.int32)
+    got = mask_gpu(par)
+    assert [int(x) for x in got[0, :, 0]] == [0x01, 0x03, 0x04, 0x0C, 0x14]
+    for T in (1, 63, 64, 65, 200, 256):
+        for par in (np.arange(-1, T - 1, dtype=np.int32)[None], np.full((1, T), -1, np.int32)):
+            assert np.array_equal(mask_gpu(par), oracle.tree_mask(par)), T
+
+
+@pytest.mark.parametrize("T", [2, 7, 16, 64, 100, 128, 255, 256])
+def test_mask_random_trees_bit_exact(T):
+    rng = np.random.default_rng(T)
+    par = np.stack([inputs.uniform_tree(rng, T) for _ in range(3)] +
+                   [inputs.bounded_tree(rng, T, 12, 4) for _ in range(3)])
+    assert np.array_equal(mask_gpu(par), oracle.tree_mask(par))
+
+
+def test_mask_bad_parent_sets_flag():
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _lib.mask_build(dev(np.array([[-1, 5, 0]], dtype=np.int32)), err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & _lib.TA_DEV_BAD_PARENT
+
+
+# ------------------------------------------------------------------------------------------------
+# fused forward, small sizes (every row checked)
+
+SMALL = [
+    ("tiny_f32", inputs.WORKLOADS["tiny_f32"], {}),
+    ("gqa_d128_ragged", wl(), {}),
+    ("gqa_d64_ragged", wl(D=64, L=(0, 300), T=12), {}),
+    ("mha_g1", wl(Hq=4, Hkv=4, T=64, L=(200, 333)), {}),
+    ("g5_two_rowblocks", wl(B=1, Hq=10, Hkv=2, T=128, L=(60, 200), depth_cap=12), {}),
+    ("g4_t128_rowblocks", wl(B=2, Hq=8, Hkv=2, T=128, L=(1, 130)), {}),
+    ("chain_t256", wl(B=1, Hq=2, Hkv=1, T=256, L=70, tree="chain"), {}),
+    ("single_node", wl(B=3, T=1, tree="single", L=(0, 129)), {}),
+    ("star", wl(B=2, T=20, tree="star", L=(64, 64)), {}),
+    ("uniform_f32_d128", wl(D=128, T=9, dtype="f32", tree="uniform", L=(1, 300)), {}),
+    ("forced_splits_1", wl(L=(300, 700)), {"num_splits": 1}),
+    ("forced_splits_7", wl(L=(300, 700)), {"num_splits": 7}),
+]
+
+
+@pytest.mark.parametrize("name,w,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_forward_small(name, w, kw):
+    for layout in ("contiguous", "paged"):
+        case = inputs.make_case(w, 0, layout=layout, page_size=16 if w.D == 64 else 64)
+        say(f"case {name} {layout} lens={case.seq_lens.tolist()}")
+        o, lse, err = run_forward(case, **kw)
+        assert err == 0
+        o_ref, lse_ref = oracle.attend_case(case)
+        check(case, o, lse, o_ref, lse_ref, f"{name}/{layout}")
+
+
+def test_unfused_calls_and_merge():
+    w = wl(B=2, Hq=8, Hkv=2, D=128, T=24, L=(0, 500), tree="uniform")
+    case = inputs.make_case(w, 3)
+    g = to_gpu(case)
+    o_c, l_c = _lib.prefix(g["q"], g["k_cache"], g["v_cache"], g["seq_lens"], scale=case.scale)
+    o_s, l_s = _lib.tree(g["q"], g["k_tree"], g["v_tree"], g["parent"], scale=case.scale)
+    o_m, l_m = _lib.merge(o_c, l_c, o_s, l_s, out_dtype=torch.float32)
+    o_b, l_b = _lib.merge(o_c, l_c, o_s, l_s, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref_c = oracle.attend_case(case, which="prefix")
+    ref_s = oracle.attend_case(case, which="tree")
+    ref = oracle.attend_case(case)
+    check(case, o_c.cpu().numpy(), l_c.cpu().numpy(), *ref_c, "prefix")
+    check(case, o_s.cpu().numpy(), l_s.cpu().numpy(), *ref_s, "tree")
+    check(case, o_m.cpu().numpy(), l_m.cpu().numpy(), *ref, "merge(prefix, tree) fp32")
+    check(case, o_b.float().cpu().numpy(), l_b.cpu().numpy(), *ref, "merge(prefix, tree) bf16")
+    # merging the oracle's own parts through the GPU merge reproduces the oracle's whole
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    sh = (2, 24, 8)
+    o_x, l_x = _lib.merge(t(ref_c[0]).view(*sh, 128), t(ref_c[1]).view(sh),
+                          t(ref_s[0]).view(*sh, 128), t(ref_s[1]).view(sh))
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(o_x.cpu().numpy().reshape(-1, 128), ref[0], atol=1e-5)
+    np.testing.assert_allclose(l_x.cpu().numpy().reshape(-1), ref[1], atol=1e-5)
+
+
+def test_merge_degenerate_parts():
+    sh = (1, 3, 2)
+    o_a = torch.randn(*sh, 64, device="cuda")
+    o_b = torch.randn(*sh, 64, device="cuda")
+    l_a = torch.randn(sh, device="cuda")
+    ninf = torch.full(sh, -float("inf"), device="cuda")
+    o, l = _lib.merge(o_a, l_a, o_b, ninf)
+    torch.cuda.synchronize()
+    assert torch.allclose(o, o_a, atol=1e-6) and torch.allclose(l, l_a, atol=1e-6)
+    o, l = _lib.merge(o_a, ninf, o_b, ninf)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isinf(l))
+
+
+def test_device_errors_set_the_flag():
+    w = wl(B=2, T=8, L=(50, 90), tree="uniform")
+    case = inputs.make_case(w, 1)
+    case.parent[1, 3] = 5                      # not topological
+    case.seq_lens[0] = case.k_cache.shape[1] + 1  # beyond the capacity
+    _, _, err = run_forward(case)
+    assert err & _lib.TA_DEV_BAD_PARENT and err & _lib.TA_DEV_BAD_LEN
+
+
+def test_determinism():
+    case = inputs.make_case(wl(L=(900, 1500)), 5)
+    o1, l1, _ = run_forward(case)
+    o2, l2, _ = run_forward(case)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ------------------------------------------------------------------------------------------------
+# full configuration sizes, sampled rows, in the default launch plan
+
+
+def sample_rows(case, n_per_b=12, seed=0):
+    rng = np.random.default_rng(seed)
+    B, T, Hq = case.wl.B, case.wl.T, case.wl.Hq
+    rows = []
+    for b in range(B):
+        picks = {(0, 0), (T - 1, Hq - 1)}
+        while len(picks) < min(n_per_b, T * Hq):
+            picks.add((int(rng.integers(T)), int(rng.integers(Hq))))
+        rows += [(b, i, h) for i, h in sorted(picks)]
+    return np.array(rows, dtype=np.int32)
+
+
+FULL = ["mha_7b", "gqa_64k", "gqa_64k_pinned", "sweep_t1", "sweep_t6", "sweep_t16", "sweep_t128",
+        "long_reasoning", "gqa_64k_beam"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size_sampled(name):
+    w = inputs.WORKLOADS[name]
+    case = inputs.make_case(w, 0)
+    say(f"full {name}: lens={case.seq_lens.tolist()}")
+    o, lse, err = run_forward(case)
+    assert err == 0
+    rows = sample_rows(case)
+    o_ref, lse_ref = oracle.attend_case(case, rows=rows)
+    B, T, Hq, D = case.q.shape
+    idx = (rows[:, 0] * T + rows[:, 1]) * Hq + rows[:, 2]
+    check(case, o.reshape(-1, D)[idx], lse.reshape(-1)[idx], o_ref, lse_ref, f"full {name}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+def test_forward_full_paged_gqa_sampled():
+    case = inputs.make_case(inputs.WORKLOADS["gqa_64k"], 1, layout="paged", page_size=64)
+    o, lse, err = run_forward(case)
+    assert err == 0
+    rows = sample_rows(case, seed=1)
+    o_ref, lse_ref = oracle.attend_case(case, rows=rows)
+    B, T, Hq, D = case.q.shape
+    idx = (rows[:, 0] * T + rows[:, 1]) * Hq + rows[:, 2]
+    check(case, o.reshape(-1, D)[idx], lse.reshape(-1)[idx], o_ref, lse_ref, "full gqa paged")

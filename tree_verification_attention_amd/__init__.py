@@ -1,0 +1,16 @@
+"""Tree-verification attention for speculative decoding on MI355X (gfx950).
+
+LongSpec's Hybrid Tree Attention: every draft-tree node attends without a mask to the committed
+KV prefix and, under an ancestor-only mask, to the other tree nodes; the two partial results are
+merged exactly through their log-sum-exps. The computation lives in hand-written HIP kernels
+behind the C ABI of ``include/treeattn.h``; this package is the thin Python binding (torch is
+used for device memory and streams only) plus the seeded synthetic-input generators.
+"""
+from ._lib import (  # noqa: F401
+    TA_BF16, TA_DEV_BAD_LEN, TA_DEV_BAD_PAGE, TA_DEV_BAD_PARENT, TA_F32, TA_MAX_TREE,
+    TreeAttnError, forward, load, make_problem, mask_build, merge, num_splits, prefix,
+    status_string, tree, workspace_size,
+)
+
+__all__ = ["forward", "prefix", "tree", "merge", "mask_build", "make_problem", "workspace_size",
+           "num_splits", "load", "status_string", "TreeAttnError"]

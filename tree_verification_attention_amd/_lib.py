@@ -1,0 +1,246 @@
+"""ctypes binding of ``libtreeattn.so`` (the C ABI declared in ``include/treeattn.h``).
+
+Argument marshalling only: torch tensors supply device pointers, strides and the current HIP
+stream; every step of the computation runs in the library's HIP kernels. There is no CPU path:
+calls raise if the library is not built or if an operand is not a GPU tensor.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtreeattn.so")
+
+TA_OK, TA_EINVAL, TA_EUNSUPPORTED, TA_EWORKSPACE, TA_EHIP = range(5)
+TA_BF16, TA_F32 = 0, 1
+TA_DEV_BAD_PARENT, TA_DEV_BAD_LEN, TA_DEV_BAD_PAGE = 1, 2, 4
+TA_MAX_TREE = 256
+
+# Functions the header declares (checked against the shared object by the test suite).
+EXPORTS = ("tree_mask_build", "tree_attn_workspace_size", "tree_attn_num_splits",
+           "tree_attn_prefix", "tree_attn_tree", "tree_attn_merge", "tree_attn_forward",
+           "tree_attn_status_string", "tree_attn_abi_version")
+
+
+class TreeAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class TaProblem(ctypes.Structure):
+    """Mirror of ``ta_problem`` (same field order, natural C alignment)."""
+
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hq", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("num_splits", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("q_sb", ctypes.c_int64), ("q_st", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("kv_s0", ctypes.c_int64), ("kv_s1", ctypes.c_int64), ("kv_s2", ctypes.c_int64),
+        ("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("Lmax", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("k_tree", ctypes.c_void_p), ("v_tree", ctypes.c_void_p),
+        ("kt_sb", ctypes.c_int64), ("kt_st", ctypes.c_int64), ("kt_sh", ctypes.c_int64),
+        ("parent", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(python tree_verification_attention_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    PP = ctypes.POINTER(TaProblem)
+    lib.tree_mask_build.argtypes = [P, I, I, P, P, P]
+    lib.tree_attn_workspace_size.argtypes = [PP, ctypes.POINTER(S)]
+    lib.tree_attn_num_splits.argtypes = [PP, ctypes.POINTER(I)]
+    lib.tree_attn_prefix.argtypes = [PP, P, P, P, S, P, P]
+    lib.tree_attn_tree.argtypes = [PP, P, P, P, P]
+    lib.tree_attn_merge.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P]
+    lib.tree_attn_forward.argtypes = [PP, P, P, P, S, P, P]
+    lib.tree_attn_status_string.argtypes = [I]
+    lib.tree_attn_status_string.restype = ctypes.c_char_p
+    lib.tree_attn_abi_version.argtypes = []
+    for fn in EXPORTS:
+        if fn not in ("tree_attn_status_string",):
+            getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().tree_attn_status_string(int(status)).decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != TA_OK:
+        raise TreeAttnError(fn, rc, status_string(rc))
+
+
+def _gpu(t: Optional[torch.Tensor], name: str, dtype=None) -> int:
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+_DT = {torch.bfloat16: TA_BF16, torch.float32: TA_F32}
+
+
+def make_problem(q, k_cache, v_cache, seq_lens, k_tree, v_tree, parent, *, block_table=None,
+                 page_size: Optional[int] = None, scale: Optional[float] = None,
+                 num_splits: int = 0) -> TaProblem:
+    """Describe one layer. Shapes: q [B,T,Hq,D]; k/v_cache [B,Lmax,Hkv,D] or, with a block
+    table [B,max_blocks], a page pool [pages,page,Hkv,D]; k/v_tree [B,T,Hkv,D]; parent [B,T];
+    seq_lens [B]. Every last dimension must be contiguous."""
+    if q.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, T, Hq, D = q.shape
+    Hkv = k_tree.shape[2] if k_tree is not None else k_cache.shape[2]
+    p = TaProblem()
+    p.B, p.T, p.Hq, p.Hkv, p.D = B, T, Hq, Hkv, D
+    p.dtype = _DT[q.dtype]
+    p.scale = float(1.0 / math.sqrt(D) if scale is None else scale)
+    p.num_splits = int(num_splits)
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_tree", k_tree),
+                    ("v_tree", v_tree)):
+        if t is not None and (t.dtype != q.dtype or t.stride(-1) != 1):
+            raise TypeError(f"{name} must be {q.dtype} with a contiguous last dimension")
+    p.q = _gpu(q, "q")
+    p.q_sb, p.q_st, p.q_sh = q.stride(0), q.stride(1), q.stride(2)
+    if k_cache is not None:
+        if tuple(k_cache.stride()) != tuple(v_cache.stride()) or k_cache.shape != v_cache.shape:
+            raise ValueError("k_cache and v_cache must share shape and strides")
+        p.k_cache = _gpu(k_cache, "k_cache")
+        p.v_cache = _gpu(v_cache, "v_cache")
+        p.kv_s0, p.kv_s1, p.kv_s2 = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+        p.seq_lens = _gpu(seq_lens, "seq_lens", torch.int32)
+        if block_table is not None:
+            p.block_table = _gpu(block_table, "block_table", torch.int32)
+            p.page_size = int(page_size if page_size is not None else k_cache.shape[1])
+            p.max_blocks = block_table.shape[1]
+            p.num_pages = k_cache.shape[0]
+            p.Lmax = 0
+        else:
+            p.Lmax = k_cache.shape[1]
+    if k_tree is not None:
+        if tuple(k_tree.stride()) != tuple(v_tree.stride()) or k_tree.shape != v_tree.shape:
+            raise ValueError("k_tree and v_tree must share shape and strides")
+        p.k_tree = _gpu(k_tree, "k_tree")
+        p.v_tree = _gpu(v_tree, "v_tree")
+        p.kt_sb, p.kt_st, p.kt_sh = k_tree.stride(0), k_tree.stride(1), k_tree.stride(2)
+        p.parent = _gpu(parent, "parent", torch.int32)
+    return p
+
+
+def workspace_size(p: TaProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check("tree_attn_workspace_size", load().tree_attn_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def num_splits(p: TaProblem) -> int:
+    n = ctypes.c_int(0)
+    _check("tree_attn_num_splits", load().tree_attn_num_splits(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(p: TaProblem, ws, device):
+    need = workspace_size(p)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def forward(q, k_cache, v_cache, seq_lens, k_tree, v_tree, parent, *, block_table=None,
+            page_size=None, scale=None, num_splits: int = 0, out=None, lse=None, workspace=None,
+            err=None):
+    """Hybrid tree attention of one layer -> (out [B,T,Hq,D] of q's dtype, lse fp32 [B,T,Hq])."""
+    p = make_problem(q, k_cache, v_cache, seq_lens, k_tree, v_tree, parent,
+                     block_table=block_table, page_size=page_size, scale=scale,
+                     num_splits=num_splits)
+    B, T, Hq, D = q.shape
+    out = torch.empty((B, T, Hq, D), dtype=q.dtype, device=q.device) if out is None else out
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    ws, nbytes = _workspace(p, workspace, q.device)
+    _check("tree_attn_forward", load().tree_attn_forward(
+        ctypes.byref(p), _gpu(out, "out", q.dtype), _gpu(lse, "lse", torch.float32),
+        _gpu(ws, "workspace"), nbytes, _gpu(err, "err", torch.int32), _stream()))
+    return out, lse
+
+
+def prefix(q, k_cache, v_cache, seq_lens, *, block_table=None, page_size=None, scale=None,
+           num_splits: int = 0, workspace=None, err=None):
+    """Unmasked attention over the committed prefix -> (o_c fp32, lse_c fp32)."""
+    p = make_problem(q, k_cache, v_cache, seq_lens, None, None, None,
+                     block_table=block_table, page_size=page_size, scale=scale,
+                     num_splits=num_splits)
+    B, T, Hq, D = q.shape
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    ws, nbytes = _workspace(p, workspace, q.device)
+    _check("tree_attn_prefix", load().tree_attn_prefix(
+        ctypes.byref(p), o.data_ptr(), lse.data_ptr(), _gpu(ws, "workspace"), nbytes,
+        _gpu(err, "err", torch.int32), _stream()))
+    return o, lse
+
+
+def tree(q, k_tree, v_tree, parent, *, scale=None, err=None):
+    """Masked attention over the tree's own keys -> (o_s fp32, lse_s fp32)."""
+    p = make_problem(q, None, None, None, k_tree, v_tree, parent, scale=scale)
+    B, T, Hq, D = q.shape
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    _check("tree_attn_tree", load().tree_attn_tree(
+        ctypes.byref(p), o.data_ptr(), lse.data_ptr(), _gpu(err, "err", torch.int32), _stream()))
+    return o, lse
+
+
+def merge(o_a, lse_a, o_b, lse_b, out_dtype=torch.float32):
+    """Log-sum-exp merge of two partial results ([B,T,Hq,D] fp32 + [B,T,Hq] fp32 each)."""
+    B, T, Hq, D = o_a.shape
+    for name, t in (("o_a", o_a), ("lse_a", lse_a), ("o_b", o_b), ("lse_b", lse_b)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        _gpu(t, name, torch.float32)
+    o = torch.empty((B, T, Hq, D), dtype=out_dtype, device=o_a.device)
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=o_a.device)
+    _check("tree_attn_merge", load().tree_attn_merge(
+        B, T, Hq, D, o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(),
+        o.data_ptr(), _DT[out_dtype], lse.data_ptr(), _stream()))
+    return o, lse
+
+
+def mask_build(parent, err=None):
+    """Ancestor-or-self masks of [B,T] int32 parents -> int64 tensor [B,T,ceil(T/64)] holding
+    the uint64 words' bit patterns."""
+    B, T = parent.shape
+    W = (T + 63) // 64
+    mask = torch.empty((B, T, W), dtype=torch.int64, device=parent.device)
+    _check("tree_mask_build", load().tree_mask_build(
+        _gpu(parent, "parent", torch.int32), B, T, mask.data_ptr(), _gpu(err, "err", torch.int32),
+        _stream()))
+    return mask

@@ -1,0 +1,298 @@
+// C ABI of the tree-verification attention library: argument checks, the split plan, workspace
+// layout and kernel launches. Every entry point only enqueues work on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "treeattn.h"
+
+namespace {
+
+using ta::AttnArgs;
+using ta::MergeArgs;
+
+constexpr int kAbiVersion = 100;
+// Workgroups the prefix launch aims for per compute unit.
+constexpr int kWgPerCu = 2;
+
+struct Plan {
+    int nw = 1;        // wavefronts per workgroup (bf16 kernel)
+    int n_rb = 1;      // row blocks per (b, kv-head)
+    int n_splits = 1;  // prefix splits
+    int chunk = ta::kKeyTile;
+    int capacity = 0;  // prefix rows addressable per sequence
+    int64_t rows = 0;  // B * T * Hq
+    size_t o_bytes = 0, lse_bytes = 0;  // workspace regions for n_splits + 1 parts
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+bool stride_ok(int64_t s, int elem) { return s >= 0 && ((s * elem) % 16) == 0; }
+
+int cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
+int elem_size(int dtype) { return dtype == TA_BF16 ? 2 : 4; }
+
+// Shape-level checks shared by every attention entry point.
+int check_shape(const ta_problem *p) {
+    if (!p) return TA_EINVAL;
+    if (p->dtype != TA_BF16 && p->dtype != TA_F32) return TA_EUNSUPPORTED;
+    if (p->D != 64 && p->D != 128) return TA_EUNSUPPORTED;
+    if (p->B < 0 || p->B > 65535 || p->T < 1 || p->T > TA_MAX_TREE) return TA_EINVAL;
+    if (p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv || p->Hkv > 4096) return TA_EINVAL;
+    if (!(p->scale > 0.f) || !isfinite(p->scale)) return TA_EINVAL;
+    if (p->num_splits < 0) return TA_EINVAL;
+    if (p->B == 0) return TA_OK;
+    const int es = elem_size(p->dtype);
+    if (!p->q || !aligned16(p->q)) return TA_EINVAL;
+    if (!stride_ok(p->q_sb, es) || !stride_ok(p->q_st, es) || !stride_ok(p->q_sh, es))
+        return TA_EINVAL;
+    return TA_OK;
+}
+
+int check_prefix(const ta_problem *p) {
+    if (p->B == 0) return TA_OK;
+    const int es = elem_size(p->dtype);
+    if (!p->seq_lens) return TA_EINVAL;
+    if (!stride_ok(p->kv_s0, es) || !stride_ok(p->kv_s1, es) || !stride_ok(p->kv_s2, es))
+        return TA_EINVAL;
+    if (p->block_table) {
+        const int ps = p->page_size;
+        if (ps < 16 || (ps & (ps - 1)) || p->max_blocks < 1 || p->num_pages < 1) return TA_EINVAL;
+        if ((int64_t)p->max_blocks * ps > INT32_MAX) return TA_EINVAL;
+    } else if (p->Lmax < 0) {
+        return TA_EINVAL;
+    }
+    if (!p->k_cache || !p->v_cache || !aligned16(p->k_cache) || !aligned16(p->v_cache))
+        return TA_EINVAL;
+    // the kernels address rows with 32-bit offsets from a per-(sequence, head) base
+    const int64_t rows = p->block_table ? p->page_size : p->Lmax;
+    if (rows * p->kv_s1 + p->D > INT32_MAX) return TA_EINVAL;
+    if (p->block_table && p->kv_s0 > INT32_MAX) return TA_EINVAL;
+    return TA_OK;
+}
+
+int check_tree(const ta_problem *p) {
+    if (p->B == 0) return TA_OK;
+    const int es = elem_size(p->dtype);
+    if (!p->parent || !p->k_tree || !p->v_tree) return TA_EINVAL;
+    if (!aligned16(p->k_tree) || !aligned16(p->v_tree)) return TA_EINVAL;
+    if (!stride_ok(p->kt_sb, es) || !stride_ok(p->kt_st, es) || !stride_ok(p->kt_sh, es))
+        return TA_EINVAL;
+    if ((int64_t)p->T * p->kt_st + p->D > INT32_MAX) return TA_EINVAL;
+    return TA_OK;
+}
+
+int ilog2(int x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return s;
+}
+
+Plan make_plan(const ta_problem *p) {
+    Plan pl;
+    const int G = p->Hq / p->Hkv;
+    const int R = p->T * G;
+    pl.capacity = p->block_table ? p->max_blocks * p->page_size : p->Lmax;
+    if (pl.capacity < 0) pl.capacity = 0;
+    pl.rows = (int64_t)p->B * p->T * p->Hq;
+    int64_t wg_per_split;
+    if (p->dtype == TA_BF16) {
+        const int rb_rows = 4 * ta::kRowsPerWave;
+        pl.n_rb = (R + rb_rows - 1) / rb_rows;
+        const int nw = (R + ta::kRowsPerWave * pl.n_rb - 1) / (ta::kRowsPerWave * pl.n_rb);
+        pl.nw = nw <= 1 ? 1 : nw <= 2 ? 2 : 4;
+        wg_per_split = (int64_t)p->B * p->Hkv * pl.n_rb;
+    } else {
+        wg_per_split = pl.rows;
+    }
+    int n = p->num_splits;
+    if (n == 0) {
+        const int64_t target = (int64_t)kWgPerCu * cu_count();
+        int64_t want = (target + wg_per_split - 1) / (wg_per_split > 0 ? wg_per_split : 1);
+        const int64_t most = (pl.capacity + 255) / 256;
+        if (want > most) want = most;
+        n = want < 1 ? 1 : (int)want;
+    }
+    int64_t chunk = pl.capacity > 0 ? ((int64_t)pl.capacity + n - 1) / n : 1;
+    chunk = (chunk + ta::kKeyTile - 1) / ta::kKeyTile * ta::kKeyTile;
+    pl.chunk = (int)chunk;
+    pl.n_splits = pl.capacity > 0 ? (int)((pl.capacity + chunk - 1) / chunk) : 1;
+    const int64_t parts = pl.n_splits + 1;
+    pl.o_bytes = align256((size_t)parts * pl.rows * p->D * sizeof(float));
+    pl.lse_bytes = align256((size_t)parts * pl.rows * sizeof(float));
+    return pl;
+}
+
+AttnArgs make_args(const ta_problem *p, const Plan &pl, int32_t *err) {
+    AttnArgs a{};
+    a.q = p->q;
+    a.q_sb = p->q_sb;
+    a.q_st = p->q_st;
+    a.q_sh = p->q_sh;
+    a.kc = p->k_cache;
+    a.vc = p->v_cache;
+    a.kv_s0 = p->kv_s0;
+    a.kv_s1 = p->kv_s1;
+    a.kv_s2 = p->kv_s2;
+    a.seq_lens = p->seq_lens;
+    a.block_table = p->block_table;
+    a.max_blocks = p->max_blocks;
+    a.page_shift = p->block_table ? ilog2(p->page_size) : 0;
+    a.page_mask = p->block_table ? p->page_size - 1 : 0;
+    a.num_pages = p->num_pages;
+    a.capacity = pl.capacity;
+    a.kt = p->k_tree;
+    a.vt = p->v_tree;
+    a.kt_sb = p->kt_sb;
+    a.kt_st = p->kt_st;
+    a.kt_sh = p->kt_sh;
+    a.parent = p->parent;
+    a.B = p->B;
+    a.T = p->T;
+    a.Hq = p->Hq;
+    a.Hkv = p->Hkv;
+    a.G = p->Hq / p->Hkv;
+    a.D = p->D;
+    a.chunk = pl.chunk;
+    a.n_rb = pl.n_rb;
+    a.scale = p->scale;
+    a.scale_log2 = p->scale * 1.4426950408889634f;
+    a.err = err;
+    return a;
+}
+
+int launch_attn(const AttnArgs &a, const Plan &pl, int dtype, hipStream_t s) {
+    const hipError_t e = dtype == TA_BF16 ? ta::launch_attn_bf16(a, pl.nw, s) : ta::launch_attn_f32(a, s);
+    return e == hipSuccess ? TA_OK : TA_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tree_attn_abi_version(void) { return kAbiVersion; }
+
+const char *tree_attn_status_string(int status) {
+    switch (status) {
+        case TA_OK: return "ok";
+        case TA_EINVAL: return "invalid argument (pointer, shape, stride, alignment or scale)";
+        case TA_EUNSUPPORTED: return "unsupported head_dim or dtype";
+        case TA_EWORKSPACE: return "workspace missing or too small";
+        case TA_EHIP: return "HIP runtime or kernel launch failure";
+        default: return "unknown status";
+    }
+}
+
+int tree_mask_build(const int32_t *parent, int B, int T, uint64_t *mask, int32_t *err_flag,
+                    hipStream_t stream) {
+    if (B < 0 || T < 1 || T > TA_MAX_TREE) return TA_EINVAL;
+    if (B == 0) return TA_OK;
+    if (!parent || !mask) return TA_EINVAL;
+    return ta::launch_mask(parent, B, T, mask, err_flag, stream) == hipSuccess ? TA_OK : TA_EHIP;
+}
+
+int tree_attn_workspace_size(const ta_problem *p, size_t *bytes) {
+    if (!bytes) return TA_EINVAL;
+    int rc = check_shape(p);
+    if (rc) return rc;
+    const Plan pl = make_plan(p);
+    *bytes = pl.o_bytes + pl.lse_bytes;
+    return TA_OK;
+}
+
+int tree_attn_num_splits(const ta_problem *p, int *num_splits) {
+    if (!num_splits) return TA_EINVAL;
+    int rc = check_shape(p);
+    if (rc) return rc;
+    *num_splits = make_plan(p).n_splits;
+    return TA_OK;
+}
+
+int tree_attn_prefix(const ta_problem *p, float *o_c, float *lse_c, void *ws, size_t ws_bytes,
+                     int32_t *err_flag, hipStream_t stream) {
+    int rc = check_shape(p);
+    if (rc) return rc;
+    if (p->B == 0) return TA_OK;
+    if ((rc = check_prefix(p))) return rc;
+    if (!o_c || !lse_c) return TA_EINVAL;
+    const Plan pl = make_plan(p);
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
+    AttnArgs a = make_args(p, pl, err_flag);
+    a.n_splits = pl.n_splits;
+    a.with_tree = 0;
+    a.out_o = static_cast<float *>(ws);
+    a.out_lse = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
+    a.part_so = pl.rows * p->D;
+    a.part_sl = pl.rows;
+    if ((rc = launch_attn(a, pl, p->dtype, stream))) return rc;
+    MergeArgs m{a.out_o, a.out_lse, a.part_so, a.part_sl, pl.n_splits, nullptr, nullptr,
+                pl.rows, p->D, o_c, lse_c};
+    return ta::launch_merge(m, false, stream) == hipSuccess ? TA_OK : TA_EHIP;
+}
+
+int tree_attn_tree(const ta_problem *p, float *o_s, float *lse_s, int32_t *err_flag,
+                   hipStream_t stream) {
+    int rc = check_shape(p);
+    if (rc) return rc;
+    if (p->B == 0) return TA_OK;
+    if ((rc = check_tree(p))) return rc;
+    if (!o_s || !lse_s) return TA_EINVAL;
+    Plan pl = make_plan(p);
+    AttnArgs a = make_args(p, pl, err_flag);
+    a.n_splits = 0;
+    a.with_tree = 1;
+    a.out_o = o_s;
+    a.out_lse = lse_s;
+    a.part_so = 0;
+    a.part_sl = 0;
+    return launch_attn(a, pl, p->dtype, stream);
+}
+
+int tree_attn_merge(int B, int T, int Hq, int D, const float *o_a, const float *lse_a,
+                    const float *o_b, const float *lse_b, void *o, int o_dtype, float *lse,
+                    hipStream_t stream) {
+    if (B < 0 || T < 0 || Hq < 0) return TA_EINVAL;
+    if (D != 64 && D != 128) return TA_EUNSUPPORTED;
+    if (o_dtype != TA_BF16 && o_dtype != TA_F32) return TA_EUNSUPPORTED;
+    const int64_t rows = (int64_t)B * T * Hq;
+    if (rows == 0) return TA_OK;
+    if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return TA_EINVAL;
+    if (((uintptr_t)o_a & 7u) || ((uintptr_t)o_b & 7u)) return TA_EINVAL;
+    MergeArgs m{o_a, lse_a, 0, 0, 1, o_b, lse_b, rows, D, o, lse};
+    return ta::launch_merge(m, o_dtype == TA_BF16, stream) == hipSuccess ? TA_OK : TA_EHIP;
+}
+
+int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t ws_bytes,
+                      int32_t *err_flag, hipStream_t stream) {
+    int rc = check_shape(p);
+    if (rc) return rc;
+    if (p->B == 0) return TA_OK;
+    if ((rc = check_prefix(p)) || (rc = check_tree(p))) return rc;
+    if (!o || !lse) return TA_EINVAL;
+    const Plan pl = make_plan(p);
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
+    AttnArgs a = make_args(p, pl, err_flag);
+    a.n_splits = pl.n_splits;
+    a.with_tree = 1;
+    a.out_o = static_cast<float *>(ws);
+    a.out_lse = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
+    a.part_so = pl.rows * p->D;
+    a.part_sl = pl.rows;
+    if ((rc = launch_attn(a, pl, p->dtype, stream))) return rc;
+    MergeArgs m{a.out_o, a.out_lse, a.part_so, a.part_sl, pl.n_splits + 1, nullptr, nullptr,
+                pl.rows, p->D, o, lse};
+    return ta::launch_merge(m, p->dtype == TA_BF16, stream) == hipSuccess ? TA_OK : TA_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal launch interface shared by the C ABI (abi.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ta {
+
+// Keys per LDS tile of the bf16 attention kernel.
+constexpr int kKeyTile = 64;
+// Packed query rows (tree node x GQA group member) handled by one wavefront.
+constexpr int kRowsPerWave = 64;
+
+// Device-side view of one attention launch. Partial outputs go to
+// out_o[part][row][D] and out_lse[part][row], row = (b * T + node) * Hq + head.
+struct AttnArgs {
+    const void *q;
+    int64_t q_sb, q_st, q_sh;
+    const void *kc, *vc;
+    int64_t kv_s0, kv_s1, kv_s2;
+    const int32_t *seq_lens;
+    const int32_t *block_table;
+    int32_t max_blocks, page_shift, page_mask, num_pages, capacity;
+    const void *kt, *vt;
+    int64_t kt_sb, kt_st, kt_sh;
+    const int32_t *parent;
+    int32_t B, T, Hq, Hkv, G, D;
+    int32_t n_splits;   // prefix parts 0..n_splits-1
+    int32_t with_tree;  // part n_splits is the masked tree part
+    int32_t chunk;      // prefix keys per split (multiple of kKeyTile)
+    int32_t n_rb;       // row blocks per (b, kv-head)
+    float scale;        // logit scale
+    float scale_log2;   // scale * log2(e)
+    float *out_o;
+    float *out_lse;
+    int64_t part_so, part_sl;  // part strides (elements) of out_o / out_lse
+    int32_t *err;
+};
+
+// Merge of n0 parts from (o0, lse0) (part strides so0 / sl0) plus, when o1 is non-null, one
+// more part (o1, lse1), into o (bf16 or fp32) and lse.
+struct MergeArgs {
+    const float *o0, *lse0;
+    int64_t so0, sl0;
+    int32_t n0;
+    const float *o1, *lse1;
+    int64_t rows;
+    int32_t D;
+    void *o;
+    float *lse;
+};
+
+hipError_t launch_mask(const int32_t *parent, int B, int T, uint64_t *mask, int32_t *err,
+                       hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs &a, int nw, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs &m, bool out_bf16, hipStream_t s);
+
+}  // namespace ta

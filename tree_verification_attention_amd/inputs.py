@@ -11,19 +11,25 @@ speculative (tree) K/V. Tree nodes are numbered in topological order (DFlash-TfM
 "Rollback-free tree verification"): parent[i] is in [-1, i-1], and -1 means the node hangs
 directly off the committed prefix.
 
-Draw order for one seed (numpy PCG64): prefix lengths -> parent arrays -> outlier channels ->
-Q -> K prefix -> V prefix -> K tree -> V tree. Values are fp32 N(0, 1), rounded to bf16 with
-round-to-nearest-even. Padding rows beyond a sequence's length are not drawn; they are filled
+For one seed, numpy PCG64(seed) draws the prefix lengths, then the parent arrays, then the
+outlier channels. Values are fp32 N(0, 1), rounded to bf16 with round-to-nearest-even; each
+value tensor (Q, K prefix, V prefix, K tree, V tree), sequence and 4096-row chunk draws from its
+own PCG64 stream seeded by SeedSequence([seed, tensor, sequence, chunk]). Padding rows beyond a sequence's length are not drawn; they are filled
 with NaN ("nan", used by tests to catch out-of-range reads) or zeros ("finite", used for timing).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
 
 BF16_NAN = np.uint16(0x7FC0)
+
+# stream keys of the value tensors
+_Q, _KP, _VP, _KT, _VT = 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -194,22 +200,43 @@ def make_tree(rng: np.random.Generator, wl: Workload) -> np.ndarray:
 # cases
 
 
-def _draw_values(rng, shape, dtype, scale_channels=None, scale=1.0, chunk_rows=1 << 14):
-    """Draw N(0,1) fp32 values of ``shape`` (leading axis chunked) and convert to ``dtype``.
+_CHUNK_ROWS = 1 << 12
+_POOL = None
 
-    ``scale_channels`` multiplies the listed last-axis channels by ``scale`` before rounding.
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        _POOL = concurrent.futures.ThreadPoolExecutor(min(16, os.cpu_count() or 1))
+    return _POOL
+
+
+def _draw_values(seed, key, shape, dtype, scale_channels=None, scale=1.0):
+    """N(0,1) fp32 values of ``shape`` converted to ``dtype`` (bf16 bits or float32).
+
+    The leading axis is cut into chunks of 4096 rows; chunk c draws from its own PCG64 stream
+    seeded by SeedSequence([seed, *key, c]), so chunks can be drawn concurrently and a value
+    never depends on the thread count. ``scale_channels`` multiplies the listed last-axis
+    channels by ``scale`` before rounding.
     """
     out_dtype = np.uint16 if dtype == "bf16" else np.float32
     out = np.empty(shape, dtype=out_dtype)
     n = shape[0]
-    for s in range(0, max(n, 1), chunk_rows):
-        e = min(n, s + chunk_rows)
-        if e <= s:
-            break
+
+    def work(c):
+        s, e = c * _CHUNK_ROWS, min(n, (c + 1) * _CHUNK_ROWS)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *key, c])))
         x = rng.standard_normal((e - s,) + tuple(shape[1:]), dtype=np.float32)
         if scale_channels is not None and len(scale_channels):
             x[..., scale_channels] *= np.float32(scale)
         out[s:e] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+    n_chunks = (n + _CHUNK_ROWS - 1) // _CHUNK_ROWS
+    if n_chunks <= 1:
+        for c in range(n_chunks):
+            work(c)
+    else:
+        list(_pool().map(work, range(n_chunks)))
     return out
 
 
@@ -244,7 +271,7 @@ def make_case(wl: Workload, seed: int = 0, *, layout: str = "contiguous", pad: s
         chans = np.sort(rng.choice(D, wl.outlier_channels, replace=False)).astype(np.int64)
 
     dt = wl.dtype
-    q = _draw_values(rng, (B * T, Hq, D), dt).reshape(B, T, Hq, D)
+    q = _draw_values(seed, (_Q, 0), (B * T, Hq, D), dt).reshape(B, T, Hq, D)
     padv = _pad_value(dt, pad)
     maxlen = int(seq_lens.max()) if B else 0
     if layout == "contiguous":
@@ -254,10 +281,10 @@ def make_case(wl: Workload, seed: int = 0, *, layout: str = "contiguous", pad: s
         kc = np.full((B, cap, Hkv, D), padv)
         vc = np.full((B, cap, Hkv, D), padv)
         for b in range(B):
-            kc[b, :seq_lens[b]] = _draw_values(rng, (int(seq_lens[b]), Hkv, D), dt, chans,
-                                               wl.outlier_scale)
+            kc[b, :seq_lens[b]] = _draw_values(seed, (_KP, b), (int(seq_lens[b]), Hkv, D), dt,
+                                               chans, wl.outlier_scale)
         for b in range(B):
-            vc[b, :seq_lens[b]] = _draw_values(rng, (int(seq_lens[b]), Hkv, D), dt)
+            vc[b, :seq_lens[b]] = _draw_values(seed, (_VP, b), (int(seq_lens[b]), Hkv, D), dt)
         block_table = None
         psz = 0
     else:
@@ -288,12 +315,13 @@ def make_case(wl: Workload, seed: int = 0, *, layout: str = "contiguous", pad: s
                 dst[block_table[b, blk], :len(rows)] = rows
 
         for b in range(B):
-            scatter(kc, b, _draw_values(rng, (int(seq_lens[b]), Hkv, D), dt, chans,
+            scatter(kc, b, _draw_values(seed, (_KP, b), (int(seq_lens[b]), Hkv, D), dt, chans,
                                         wl.outlier_scale))
         for b in range(B):
-            scatter(vc, b, _draw_values(rng, (int(seq_lens[b]), Hkv, D), dt))
-    kt = _draw_values(rng, (B * T, Hkv, D), dt, chans, wl.outlier_scale).reshape(B, T, Hkv, D)
-    vt = _draw_values(rng, (B * T, Hkv, D), dt).reshape(B, T, Hkv, D)
+            scatter(vc, b, _draw_values(seed, (_VP, b), (int(seq_lens[b]), Hkv, D), dt))
+    kt = _draw_values(seed, (_KT, 0), (B * T, Hkv, D), dt, chans,
+                      wl.outlier_scale).reshape(B, T, Hkv, D)
+    vt = _draw_values(seed, (_VT, 0), (B * T, Hkv, D), dt).reshape(B, T, Hkv, D)
     return Case(wl=wl, seed=seed, seq_lens=seq_lens, parent=par, q=q, k_cache=kc, v_cache=vc,
                 k_tree=kt, v_tree=vt, block_table=block_table, page_size=psz, lcap=cap,
                 outlier_channels=chans)
