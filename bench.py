@@ -1,0 +1,362 @@
+#!/usr/bin/env python3
+"""Tree-verification attention benchmark on one MI355X.
+
+Headline workload: one GQA bf16 attention layer of a speculative-decoding verify step -- B = 4
+sequences, 32 query heads over 8 KV heads, head_dim 128, a 64-node draft tree per sequence
+(depth <= 8, at most 4 children per node) and a 65536-token committed prefix per sequence.
+Inputs are seeded synthetic values (see tree_verification_attention_amd.inputs), copied to HBM
+before the timed region.
+
+A step is one call of tree_attn_forward: all prefix splits plus the masked tree part, then the
+log-sum-exp combine. ``value`` is the achieved algorithmic HBM bandwidth of a step (prefix K/V,
+Q, tree K/V and parents read once; O and LSE written once) in TB/s; ``us_per_layer`` is the
+same step's time. The roofline entry is for the dominant kernel (the split/tree attention
+kernel, launched alone through tree_attn_partials and timed with HIP events on its stream).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --parse-pmc FETCH_DIR WRITE_DIR   (writes the traffic summary)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tree-verify attention µs/layer + achieved HBM TB/s, 64-node tree @64k ctx"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+KERNEL_NAME = "attn_bf16_kernel"
+COPY_BYTES = 1 << 30
+CSRC = os.path.join(ROOT, "tree_verification_attention_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def work_of(case):
+    """Algorithmic bytes and flops of one layer (and of its dominant kernel)."""
+    wl = case.wl
+    es = 2 if wl.dtype == "bf16" else 4
+    B, T, Hq, Hkv, D = wl.B, wl.T, wl.Hq, wl.Hkv, wl.D
+    sum_l = int(case.seq_lens.astype("int64").sum())
+    kv = 2 * es * Hkv * D * sum_l
+    q = es * B * T * Hq * D
+    tree = 2 * es * B * T * Hkv * D
+    meta = 4 * B * T + 4 * B
+    if case.block_table is not None:
+        ps = case.page_size
+        meta += 4 * int(sum((int(n) + ps - 1) // ps for n in case.seq_lens))
+    out = es * B * T * Hq * D + 4 * B * T * Hq
+    from tree_verification_attention_amd.inputs import tree_depths
+    visible_tree = int(sum(tree_depths(case.parent[b]).sum() for b in range(B)))
+    flops = 4 * D * Hq * (T * sum_l + visible_tree)
+    return {"kernel_bytes": kv + q + tree + meta, "step_bytes": kv + q + tree + meta + out,
+            "flops": flops, "sum_len": sum_l}
+
+
+def to_device(case):
+    import numpy as np
+    import torch
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    return {k: dev(getattr(case, k)) for k in ("q", "k_cache", "v_cache", "seq_lens", "k_tree",
+                                                "v_tree", "parent", "block_table")}
+
+
+def time_case(case, steps, warmup, label):
+    """Time ``steps`` fused forwards and ``steps`` dominant-kernel launches of ``case``."""
+    import ctypes
+
+    import torch
+
+    from tree_verification_attention_amd import _lib
+
+    g = to_device(case)
+    p = _lib.make_problem(g["q"], g["k_cache"], g["v_cache"], g["seq_lens"], g["k_tree"],
+                          g["v_tree"], g["parent"], block_table=g["block_table"],
+                          page_size=case.page_size or None, scale=case.scale)
+    lib = _lib.load()
+    B, T, Hq, D = case.q.shape
+    out = torch.empty((B, T, Hq, D), dtype=g["q"].dtype, device="cuda")
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
+    ws_bytes = _lib.workspace_size(p)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    pp = ctypes.byref(p)
+    args_fwd = (pp, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws_bytes, err.data_ptr(), sh)
+    args_part = (pp, ws.data_ptr(), ws_bytes, err.data_ptr(), sh)
+
+    def fwd():
+        rc = lib.tree_attn_forward(*args_fwd)
+        if rc:
+            raise RuntimeError(f"tree_attn_forward: {_lib.status_string(rc)}")
+
+    def part():
+        rc = lib.tree_attn_partials(*args_part)
+        if rc:
+            raise RuntimeError(f"tree_attn_partials: {_lib.status_string(rc)}")
+
+    print(f"[bench] {label}: warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` fused steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    # the dominant kernel alone, same stream, same events
+    for _ in range(warmup):
+        part()
+    torch.cuda.synchronize()
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        kev[i][0].record(stream)
+        part()
+        kev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_us = [a.elapsed_time(b) * 1e3 for a, b in kev]
+    flag = int(err.item())
+    if flag:
+        raise RuntimeError(f"device error flag {flag}")
+    print(f"[bench] {label}: done ({wall * 1e3 / steps:.1f} us/step wall)", file=sys.stderr,
+          flush=True)
+    return {"wall_s": wall, "step_us": step_us, "kernel_us": kern_us,
+            "n_splits": _lib.num_splits(p), "ws_bytes": ws_bytes}
+
+
+def pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+
+def cpu_baseline(case, threads):
+    """The oracle on a bounded sample: every node and head of sequence 0."""
+    import numpy as np
+
+    import oracle
+
+    wl = case.wl
+    rows = np.array([(0, i, h) for i in range(wl.T) for h in range(wl.Hq)], dtype=np.int32)
+    print(f"[bench] cpu baseline: {len(rows)} rows on {threads} threads", file=sys.stderr,
+          flush=True)
+    t0 = time.perf_counter()
+    oracle.attend_case(case, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    es = 2 if wl.dtype == "bf16" else 4
+    L0 = int(case.seq_lens[0])
+    sample_bytes = (2 * es * wl.Hkv * wl.D * L0 + es * wl.T * wl.Hq * wl.D
+                    + 2 * es * wl.T * wl.Hkv * wl.D + 4 * wl.T + es * wl.T * wl.Hq * wl.D
+                    + 4 * wl.T * wl.Hq)
+    return {"value": sample_bytes / dt / 1e12, "unit": "TB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"sequence 0 of {wl.B}: all {wl.T} nodes x {wl.Hq} q-heads over its "
+                      f"{L0}-token prefix and tree ({len(rows)} rows), fp64 two-pass softmax",
+            "seconds": round(dt, 3),
+            "us_per_layer_extrapolated": round(dt * 1e6 * int(case.seq_lens.sum()) / max(L0, 1), 1)}
+
+
+def traffic_entry(workload):
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha256") != kernel_source_hash():
+        return None   # the kernel changed since the counters were taken
+    return t
+
+
+def copy_calibration(n=5):
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(n):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def parse_pmc(fetch_dir, write_dir, workload):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the attention and copy kernels, scaled by
+    what the counters read for a plain copy of known size."""
+
+    def read(d, counter):
+        vals = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    name = row["Kernel_Name"]
+                    vals.setdefault(name, []).append(float(row["Counter_Value"]))
+        return vals
+
+    def pick(vals, needle):
+        keys = [k for k in vals if needle in k]
+        if not keys:
+            raise SystemExit(f"no dispatches of {needle} in counters: {list(vals)[:8]}")
+        xs = [v for k in keys for v in vals[k]]
+        return statistics.mean(xs), len(xs), keys[0]
+
+    fetch = read(fetch_dir, "FETCH_SIZE")
+    write = read(write_dir, "WRITE_SIZE")
+    kf, nkf, kname = pick(fetch, KERNEL_NAME)
+    kw, _, _ = pick(write, KERNEL_NAME)
+    # the plain copy: the dispatch whose name mentions copy and whose fetch is largest
+    copies = {k: v for k, v in fetch.items() if "copy" in k.lower() or "elementwise" in k.lower()}
+    cname = max(copies, key=lambda k: statistics.mean(copies[k]))
+    cf = statistics.mean(fetch[cname])
+    cw = statistics.mean(write.get(cname, [0.0]))
+    f_scale = COPY_BYTES / (cf * 1024.0)
+    w_scale = COPY_BYTES / (cw * 1024.0) if cw else float("nan")
+    entry = {"workload": workload, "kernel": kname, "dispatches": nkf,
+             "fetch_kib": kf, "write_kib": kw, "copy_kernel": cname, "copy_fetch_kib": cf,
+             "copy_write_kib": cw, "fetch_scale": f_scale, "write_scale": w_scale,
+             "fetch_bytes": kf * 1024.0 * f_scale, "write_bytes": kw * 1024.0 * w_scale,
+             "kernel_src_sha256": kernel_source_hash()}
+    entry["traffic_bytes"] = entry["fetch_bytes"] + entry["write_bytes"]
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"traffic_{workload}.json")
+    with open(out, "w") as f:
+        json.dump(entry, f, indent=1)
+    print(json.dumps(entry, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa_64k_pinned")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the drawn-length (32k..64k) variant of the workload")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain 1 GiB copies (reference for HBM counters)")
+    ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.parse_pmc:
+        parse_pmc(args.parse_pmc[0], args.parse_pmc[1], args.workload)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the tree-attention path here is single-device "
+              "(its sharding across GPUs is a design note, not built); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from tree_verification_attention_amd import _lib, inputs
+
+    _lib.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    wl = inputs.WORKLOADS[args.workload]
+    print(f"[bench] generating {wl.name} (seed {args.seed})", file=sys.stderr, flush=True)
+    case = inputs.make_case(wl, args.seed, pad="finite")
+    work = work_of(case)
+    res = time_case(case, args.steps, args.warmup, wl.name)
+
+    ms_per_step = res["wall_s"] * 1e3 / args.steps
+    value = work["step_bytes"] / (ms_per_step * 1e-3) / 1e12
+    kern_avg_us = statistics.mean(res["kernel_us"])
+    achieved = work["kernel_bytes"] / (kern_avg_us * 1e-6) / 1e9
+    traffic = traffic_entry(wl.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) values rounded to bf16, bounded-random trees)",
+        "config": {"workload": "GQA bf16, 64-node tree, every prefix 64k tokens", "name": wl.name,
+                   "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.D,
+                   "tree_nodes": wl.T, "prefix_lens": case.seq_lens.tolist(),
+                   "tree": f"{wl.tree}, depth<={wl.depth_cap}, children<={wl.branch_cap}",
+                   "layout": "contiguous [B, L, Hkv, D]", "kv_splits": res["n_splits"]},
+        "us_per_layer": round(ms_per_step * 1e3, 2),
+        "us_per_layer_events": {"p10": round(pct(res["step_us"], 0.1), 2),
+                                "median": round(pct(res["step_us"], 0.5), 2),
+                                "p90": round(pct(res["step_us"], 0.9), 2)},
+        "node_qheads_per_s": wl.B * wl.T * wl.Hq / (ms_per_step * 1e-3),
+        "prefix_token_kvheads_per_s": work["sum_len"] * wl.Hkv / (ms_per_step * 1e-3),
+        "algorithmic_bytes_per_step": work["step_bytes"],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic["traffic_bytes"] if traffic else None,
+                     "kernel": KERNEL_NAME, "kernel_avg_us": round(kern_avg_us, 2),
+                     "kernel_bytes": work["kernel_bytes"]},
+        "mfma": {"achieved_tflops": round(work["flops"] / (kern_avg_us * 1e-6) / 1e12, 1),
+                 "peak_tflops": MFMA_BF16_PEAK_TFS,
+                 "frac": round(work["flops"] / (kern_avg_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+                 "flops_per_step": work["flops"]},
+    }
+    torch.cuda.empty_cache()
+    if not args.no_secondary and wl.name == "gqa_64k_pinned":
+        wl2 = inputs.WORKLOADS["gqa_64k"]
+        case2 = inputs.make_case(wl2, args.seed, pad="finite")
+        w2 = work_of(case2)
+        r2 = time_case(case2, args.steps, args.warmup, wl2.name)
+        ms2 = r2["wall_s"] * 1e3 / args.steps
+        line["secondary"] = {"workload": "GQA bf16, 64-node tree, prefix lengths drawn in [32k, 64k]",
+                             "prefix_lens": case2.seq_lens.tolist(),
+                             "us_per_layer": round(ms2 * 1e3, 2),
+                             "tb_per_s": round(w2["step_bytes"] / (ms2 * 1e-3) / 1e12, 4),
+                             "kernel_avg_us": round(statistics.mean(r2["kernel_us"]), 2)}
+        del case2
+        torch.cuda.empty_cache()
+    if args.copy_calibration:
+        copy_calibration()
+    if not args.no_cpu_baseline:
+        threads = min(16, len(os.sched_getaffinity(0)))
+        line["cpu_baseline"] = cpu_baseline(case, threads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

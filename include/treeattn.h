@@ -115,7 +115,7 @@ int tree_mask_build(const int32_t *parent, int B, int T, uint64_t *mask, int32_t
 
 /*
  * Host-only. Bytes of workspace that tree_attn_prefix and tree_attn_forward need for ``p``
- * (the per-split partial outputs and log-sum-exps, fp32). Writes *bytes; returns TA_EINVAL /
+ * (one partial output and log-sum-exp per split, fp32). Writes *bytes; returns TA_EINVAL /
  * TA_EUNSUPPORTED for a problem the other calls would reject.
  */
 int tree_attn_workspace_size(const ta_problem *p, size_t *bytes);
@@ -158,10 +158,34 @@ int tree_attn_merge(int B, int T, int Hq, int D, const float *o_a, const float *
 /*
  * The whole hybrid tree attention of one layer: prefix (split over the KV length), masked tree
  * part with the mask derived in-kernel, and the log-sum-exp aggregation of all partials, in two
- * launches. o: [B, T, Hq, D] contiguous, of p->dtype; lse: fp32 [B, T, Hq] (natural log).
+ * launches (tree_attn_partials, then tree_attn_combine). o: [B, T, Hq, D] contiguous, of
+ * p->dtype; lse: fp32 [B, T, Hq] (natural log).
  */
 int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t ws_bytes,
                       int32_t *err_flag, hipStream_t stream);
+
+/*
+ * The divide step of tree_attn_forward on its own: every prefix split and the masked tree part
+ * write their partial (O, LSE) into ``ws`` (LongSpec page, "Fast tree attention", splitting the
+ * key-value pairs; the prefix is further split along its length). Workspace layout, with
+ * P = tree_attn_num_splits() parts and rows = B * T * Hq: fp32 O parts [P][rows][D] at byte 0,
+ * then fp32 LSE parts [P][rows] at byte tree_attn_workspace_lse_offset(). Part p covers one
+ * chunk of every sequence's prefix; the last part also covers the masked tree keys. A caller
+ * that shards the prefix over several devices exchanges these partials.
+ */
+int tree_attn_partials(const ta_problem *p, void *ws, size_t ws_bytes, int32_t *err_flag,
+                       hipStream_t stream);
+
+/*
+ * The aggregation step on its own: merges the P parts that tree_attn_partials left in ``ws``
+ * (same ``p``) by the log-sum-exp identity into o ([B, T, Hq, D], p->dtype) and lse (fp32).
+ * tree_attn_forward == tree_attn_partials followed by tree_attn_combine.
+ */
+int tree_attn_combine(const ta_problem *p, const void *ws, size_t ws_bytes, void *o, float *lse,
+                      hipStream_t stream);
+
+/* Host-only. Byte offset of the LSE parts inside the workspace of ``p``. */
+int tree_attn_workspace_lse_offset(const ta_problem *p, size_t *offset);
 
 /* Static description of a status code. Never NULL. */
 const char *tree_attn_status_string(int status);

@@ -24,6 +24,7 @@ TA_MAX_TREE = 256
 # Functions the header declares (checked against the shared object by the test suite).
 EXPORTS = ("tree_mask_build", "tree_attn_workspace_size", "tree_attn_num_splits",
            "tree_attn_prefix", "tree_attn_tree", "tree_attn_merge", "tree_attn_forward",
+           "tree_attn_partials", "tree_attn_combine", "tree_attn_workspace_lse_offset",
            "tree_attn_status_string", "tree_attn_abi_version")
 
 
@@ -74,6 +75,9 @@ def load(path: str = LIB_PATH):
     lib.tree_attn_tree.argtypes = [PP, P, P, P, P]
     lib.tree_attn_merge.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P]
     lib.tree_attn_forward.argtypes = [PP, P, P, P, S, P, P]
+    lib.tree_attn_partials.argtypes = [PP, P, S, P, P]
+    lib.tree_attn_combine.argtypes = [PP, P, S, P, P, P]
+    lib.tree_attn_workspace_lse_offset.argtypes = [PP, ctypes.POINTER(S)]
     lib.tree_attn_status_string.argtypes = [I]
     lib.tree_attn_status_string.restype = ctypes.c_char_p
     lib.tree_attn_abi_version.argtypes = []
@@ -190,6 +194,28 @@ def forward(q, k_cache, v_cache, seq_lens, k_tree, v_tree, parent, *, block_tabl
         ctypes.byref(p), _gpu(out, "out", q.dtype), _gpu(lse, "lse", torch.float32),
         _gpu(ws, "workspace"), nbytes, _gpu(err, "err", torch.int32), _stream()))
     return out, lse
+
+
+def partials(p: TaProblem, workspace, err=None):
+    """Launch the divide step (all prefix splits and the tree part) of problem ``p`` into
+    ``workspace``; see tree_attn_partials for the workspace layout."""
+    _check("tree_attn_partials", load().tree_attn_partials(
+        ctypes.byref(p), _gpu(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _gpu(err, "err", torch.int32), _stream()))
+
+
+def combine(p: TaProblem, workspace, out, lse):
+    """Launch the aggregation of the parts in ``workspace`` into ``out`` / ``lse``."""
+    _check("tree_attn_combine", load().tree_attn_combine(
+        ctypes.byref(p), _gpu(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _gpu(out, "out"), _gpu(lse, "lse", torch.float32), _stream()))
+
+
+def workspace_lse_offset(p: TaProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check("tree_attn_workspace_lse_offset",
+           load().tree_attn_workspace_lse_offset(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
 
 
 def prefix(q, k_cache, v_cache, seq_lens, *, block_table=None, page_size=None, scale=None,

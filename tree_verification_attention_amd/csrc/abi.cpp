@@ -15,7 +15,7 @@ using ta::MergeArgs;
 
 constexpr int kAbiVersion = 100;
 // Workgroups the prefix launch aims for per compute unit.
-constexpr int kWgPerCu = 2;
+constexpr int kWgPerCu = 1;
 
 struct Plan {
     int nw = 1;        // wavefronts per workgroup (bf16 kernel)
@@ -24,7 +24,7 @@ struct Plan {
     int chunk = ta::kKeyTile;
     int capacity = 0;  // prefix rows addressable per sequence
     int64_t rows = 0;  // B * T * Hq
-    size_t o_bytes = 0, lse_bytes = 0;  // workspace regions for n_splits + 1 parts
+    size_t o_bytes = 0, lse_bytes = 0;  // workspace regions for n_splits parts
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -128,7 +128,7 @@ Plan make_plan(const ta_problem *p) {
     chunk = (chunk + ta::kKeyTile - 1) / ta::kKeyTile * ta::kKeyTile;
     pl.chunk = (int)chunk;
     pl.n_splits = pl.capacity > 0 ? (int)((pl.capacity + chunk - 1) / chunk) : 1;
-    const int64_t parts = pl.n_splits + 1;
+    const int64_t parts = pl.n_splits;
     pl.o_bytes = align256((size_t)parts * pl.rows * p->D * sizeof(float));
     pl.lse_bytes = align256((size_t)parts * pl.rows * sizeof(float));
     return pl;
@@ -230,6 +230,7 @@ int tree_attn_prefix(const ta_problem *p, float *o_c, float *lse_c, void *ws, si
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
     AttnArgs a = make_args(p, pl, err_flag);
     a.n_splits = pl.n_splits;
+    a.with_prefix = 1;
     a.with_tree = 0;
     a.out_o = static_cast<float *>(ws);
     a.out_lse = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
@@ -250,7 +251,8 @@ int tree_attn_tree(const ta_problem *p, float *o_s, float *lse_s, int32_t *err_f
     if (!o_s || !lse_s) return TA_EINVAL;
     Plan pl = make_plan(p);
     AttnArgs a = make_args(p, pl, err_flag);
-    a.n_splits = 0;
+    a.n_splits = 1;
+    a.with_prefix = 0;
     a.with_tree = 1;
     a.out_o = o_s;
     a.out_lse = lse_s;
@@ -273,26 +275,56 @@ int tree_attn_merge(int B, int T, int Hq, int D, const float *o_a, const float *
     return ta::launch_merge(m, o_dtype == TA_BF16, stream) == hipSuccess ? TA_OK : TA_EHIP;
 }
 
-int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t ws_bytes,
-                      int32_t *err_flag, hipStream_t stream) {
+int tree_attn_workspace_lse_offset(const ta_problem *p, size_t *offset) {
+    if (!offset) return TA_EINVAL;
+    int rc = check_shape(p);
+    if (rc) return rc;
+    *offset = make_plan(p).o_bytes;
+    return TA_OK;
+}
+
+int tree_attn_partials(const ta_problem *p, void *ws, size_t ws_bytes, int32_t *err_flag,
+                       hipStream_t stream) {
     int rc = check_shape(p);
     if (rc) return rc;
     if (p->B == 0) return TA_OK;
     if ((rc = check_prefix(p)) || (rc = check_tree(p))) return rc;
-    if (!o || !lse) return TA_EINVAL;
     const Plan pl = make_plan(p);
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
     AttnArgs a = make_args(p, pl, err_flag);
     a.n_splits = pl.n_splits;
+    a.with_prefix = 1;
     a.with_tree = 1;
     a.out_o = static_cast<float *>(ws);
     a.out_lse = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
     a.part_so = pl.rows * p->D;
     a.part_sl = pl.rows;
-    if ((rc = launch_attn(a, pl, p->dtype, stream))) return rc;
-    MergeArgs m{a.out_o, a.out_lse, a.part_so, a.part_sl, pl.n_splits + 1, nullptr, nullptr,
+    return launch_attn(a, pl, p->dtype, stream);
+}
+
+int tree_attn_combine(const ta_problem *p, const void *ws, size_t ws_bytes, void *o, float *lse,
+                      hipStream_t stream) {
+    int rc = check_shape(p);
+    if (rc) return rc;
+    if (p->B == 0) return TA_OK;
+    if (!o || !lse) return TA_EINVAL;
+    const Plan pl = make_plan(p);
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
+    const float *wo = static_cast<const float *>(ws);
+    const float *wl = reinterpret_cast<const float *>(static_cast<const char *>(ws) + pl.o_bytes);
+    MergeArgs m{wo, wl, pl.rows * p->D, pl.rows, pl.n_splits, nullptr, nullptr,
                 pl.rows, p->D, o, lse};
     return ta::launch_merge(m, p->dtype == TA_BF16, stream) == hipSuccess ? TA_OK : TA_EHIP;
+}
+
+int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t ws_bytes,
+                      int32_t *err_flag, hipStream_t stream) {
+    int rc = check_shape(p);
+    if (rc) return rc;
+    if (p->B == 0) return TA_OK;
+    if (!o || !lse) return TA_EINVAL;
+    if ((rc = tree_attn_partials(p, ws, ws_bytes, err_flag, stream))) return rc;
+    return tree_attn_combine(p, ws, ws_bytes, o, lse, stream);
 }
 
 }  // extern "C"

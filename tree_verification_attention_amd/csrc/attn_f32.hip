@@ -1,7 +1,7 @@
 // fp32 attention parts for tree verification (the fp32-input path).
 //
-// Same partial outputs as the bf16 kernel -- one (O, LSE) per (part, row) for a prefix chunk or
-// for the masked tree -- computed with plain fp32 vector arithmetic: there is no fp32 MFMA
+// Same partial outputs as the bf16 kernel -- one (O, LSE) per (part, row) for a prefix chunk,
+// plus the masked tree keys in the last part -- computed with plain fp32 vector arithmetic: there is no fp32 MFMA
 // shape worth using at these sizes. One wavefront per (row, part); every lane walks its own
 // subset of keys with an online softmax, then the 64 lane partials are merged through LDS by the
 // log-sum-exp identity.
@@ -28,52 +28,55 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     const int node = (int)((row / a.Hq) % a.T);
     const int b = (int)(row / ((int64_t)a.Hq * a.T));
     const int g = h / a.G;
-    const bool tree = a.with_tree && part == a.n_splits;
+    const bool has_tree = a.with_tree && part == a.n_splits - 1;
 
     const float *q = reinterpret_cast<const float *>(a.q) + b * a.q_sb + node * a.q_st + h * a.q_sh;
     for (int d = lane; d < D; d += 64) qs[d] = q[d];
 
-    int k_begin = 0, k_end;
-    if (tree) {
-        k_end = a.T;
-        // ancestor-or-self bitmap of `node`, walked upwards from the node itself
-        for (int w = lane; w < TA_MAX_TREE / 32; w += 64) anc[w] = 0u;
-        __syncthreads();
-        if (lane == 0) {
-            const int32_t *par = a.parent + (int64_t)b * a.T;
-            int j = node;
-            while (j >= 0) {
-                anc[j >> 5] |= 1u << (j & 31);
-                const int p = par[j];
-                if (p < -1 || p >= j) {
-                    if (a.err) atomicOr(a.err, (int32_t)TA_DEV_BAD_PARENT);
-                    break;
-                }
-                j = p;
-            }
-        }
-    } else {
+    // prefix keys [pb, pe) of this part
+    int pb = 0, pe = 0;
+    if (a.with_prefix) {
         int L = a.seq_lens[b];
         if (L < 0 || L > a.capacity) {
             if (a.err && lane == 0) atomicOr(a.err, (int32_t)TA_DEV_BAD_LEN);
             L = L < 0 ? 0 : a.capacity;
         }
-        k_begin = part * a.chunk;
-        k_end = min(k_begin + a.chunk, L);
+        pb = part * a.chunk;
+        pe = min(pb + a.chunk, L);
+        if (pe < pb) pe = pb;
+    }
+    // ancestor-or-self bitmap of `node`, walked upwards from the node itself
+    for (int w = lane; w < TA_MAX_TREE / 32; w += 64) anc[w] = 0u;
+    __syncthreads();
+    if (has_tree && lane == 0) {
+        const int32_t *par = a.parent + (int64_t)b * a.T;
+        int j = node;
+        while (j >= 0) {
+            anc[j >> 5] |= 1u << (j & 31);
+            const int p = par[j];
+            if (p < -1 || p >= j) {
+                if (a.err) atomicOr(a.err, (int32_t)TA_DEV_BAD_PARENT);
+                break;
+            }
+            j = p;
+        }
     }
     __syncthreads();
 
     float m = -INFINITY, l = 0.f, acc[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) acc[d] = 0.f;
-    for (int j = k_begin + lane; j < k_end; j += 64) {
+    const int n_keys = (pe - pb) + (has_tree ? a.T : 0);
+    for (int k = lane; k < n_keys; k += 64) {
         const float *kp, *vp;
-        if (tree) {
+        if (k >= pe - pb) {
+            const int j = k - (pe - pb);
             if (!((anc[j >> 5] >> (j & 31)) & 1u)) continue;
             const int64_t off = b * a.kt_sb + j * a.kt_st + g * a.kt_sh;
             kp = reinterpret_cast<const float *>(a.kt) + off;
             vp = reinterpret_cast<const float *>(a.vt) + off;
         } else {
+            const int j = pb + k;
             int64_t off;
             if (a.block_table) {
                 const int pg = a.block_table[(int64_t)b * a.max_blocks + (j >> a.page_shift)];
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 }
 
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s) {
-    const int parts = a.n_splits + (a.with_tree ? 1 : 0);
+    const int parts = a.n_splits;
     const int64_t rows = (int64_t)a.B * a.T * a.Hq;
     if (parts == 0 || rows == 0) return hipSuccess;
     const dim3 grid((unsigned)rows, parts);

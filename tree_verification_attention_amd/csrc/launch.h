@@ -6,12 +6,14 @@
 
 namespace ta {
 
-// Keys per LDS tile of the bf16 attention kernel.
+// Keys per LDS tile of the bf16 attention kernel (two 32-key MFMA sub-tiles).
 constexpr int kKeyTile = 64;
 // Packed query rows (tree node x GQA group member) handled by one wavefront.
 constexpr int kRowsPerWave = 64;
 
-// Device-side view of one attention launch. Partial outputs go to
+// Device-side view of one attention launch. Part p (0 <= p < n_splits) covers prefix keys
+// [p * chunk, min((p + 1) * chunk, seq_len)) when with_prefix is set, and the last part also
+// covers the masked tree keys when with_tree is set. Partial outputs go to
 // out_o[part][row][D] and out_lse[part][row], row = (b * T + node) * Hq + head.
 struct AttnArgs {
     const void *q;
@@ -25,8 +27,9 @@ struct AttnArgs {
     int64_t kt_sb, kt_st, kt_sh;
     const int32_t *parent;
     int32_t B, T, Hq, Hkv, G, D;
-    int32_t n_splits;   // prefix parts 0..n_splits-1
-    int32_t with_tree;  // part n_splits is the masked tree part
+    int32_t n_splits;
+    int32_t with_prefix;
+    int32_t with_tree;
     int32_t chunk;      // prefix keys per split (multiple of kKeyTile)
     int32_t n_rb;       // row blocks per (b, kv-head)
     float scale;        // logit scale
