@@ -127,8 +127,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     }
 
     // ---- KV tile staging: HBM -> registers -> LDS. Thread t moves 16-byte chunk (t % DCH) of
-    // key rows t / DCH, t / DCH + NT / DCH, ...; rows past the end of the range read a valid row
-    // and are replaced by zeros.
+    // key rows t / DCH, t / DCH + NT / DCH, ...; a row past the end of the range loads the last
+    // valid row instead (finite data), and its scores are masked to -inf so it adds nothing.
     const __bf16 *kc_bg = reinterpret_cast<const __bf16 *>(a.kc) +
                           (PAGED ? 0 : b * a.kv_s0) + g * a.kv_s2;
     const __bf16 *vc_bg = reinterpret_cast<const __bf16 *>(a.vc) +
@@ -136,9 +136,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     const __bf16 *kt_bg = reinterpret_cast<const __bf16 *>(a.kt) + b * a.kt_sb + g * a.kt_sh;
     const __bf16 *vt_bg = reinterpret_cast<const __bf16 *>(a.vt) + b * a.kt_sb + g * a.kt_sh;
     const int pstride = (int)a.kv_s1, tstride = (int)a.kt_st, page_stride = (int)a.kv_s0;
-    u32x4 stK[NLOAD], stV[NLOAD];
+    u32x4 stA_K[NLOAD], stA_V[NLOAD];
+    u32x4 stB_K[NW == 4 ? NLOAD : 1], stB_V[NW == 4 ? NLOAD : 1];
 
-    auto load_tile = [&](int t) {
+    auto load_tile = [&](int t, u32x4 (&stK)[NLOAD], u32x4 (&stV)[NLOAD]) __attribute__((always_inline)) {
         const bool tree_tile = t >= n_ptiles;
         const int k0 = tree_tile ? (t - n_ptiles) * KT : pb + t * KT;
         const int kend = tree_tile ? a.T : pe;
@@ -148,8 +149,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
         for (int i = 0; i < NLOAD; ++i) {
             const int c = tid + i * NT;
             const int row = c / DCH, ch = c % DCH;
-            const int key = k0 + row;
-            const int kc = min(key, kend - 1);
+            const int kc = min(k0 + row, kend - 1);
             int64_t off;
             if (tree_tile) {
                 off = kc * tstride;
@@ -160,18 +160,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
             } else {
                 off = kc * pstride;
             }
-            u32x4 kv = *reinterpret_cast<const u32x4 *>(kb + off + ch * 8);
-            u32x4 vv = *reinterpret_cast<const u32x4 *>(vb + off + ch * 8);
-            if (key >= kend) {
-                kv = u32x4{0u, 0u, 0u, 0u};
-                vv = u32x4{0u, 0u, 0u, 0u};
-            }
-            stK[i] = kv;
-            stV[i] = vv;
+            stK[i] = *reinterpret_cast<const u32x4 *>(kb + off + ch * 8);
+            stV[i] = *reinterpret_cast<const u32x4 *>(vb + off + ch * 8);
         }
     };
 
-    auto store_tile = [&](int s) {
+    auto store_tile = [&](int s, const u32x4 (&stK)[NLOAD], const u32x4 (&stV)[NLOAD]) __attribute__((always_inline)) {
         uint16_t *Ks = smem + s * STAGE;
         uint16_t *Vs = Ks + TILE;
 #pragma unroll
@@ -186,7 +180,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     // ---- accumulators and softmax state
     f32x16 acc[2][DT];
     float m_run[2], l_run[2];
-    auto reset_state = [&]() {
+    auto reset_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
@@ -212,7 +206,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     const int v_sw = v_row << 1;
 
     // S^T for one 32-key block (jb) of the stage
-    auto qk = [&](const uint16_t *Ks, int jb, f32x16 (&S)[2]) {
+    auto qk = [&](const uint16_t *Ks, int jb, f32x16 (&S)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
@@ -228,7 +222,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     };
 
     // O^T += V^T P^T for one 32-key block
-    auto pv = [&](const uint16_t *Vs, int jb, const bf16x8 (&P)[2][2]) {
+    auto pv = [&](const uint16_t *Vs, int jb, const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int key0 = jb * 32 + u * 16 + v_hfk;  // second key group: key0 + 8
@@ -254,7 +248,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
 
     // Mask the scores of one 32-key block in place. Key of register r: jb*32 + 8*(r/4) + 4*hf
     // + r%4 inside the tile.
-    auto mask_block = [&](f32x16 (&S)[2], int t, int jb) {
+    auto mask_block = [&](f32x16 (&S)[2], int t, int jb) __attribute__((always_inline)) {
         if (t >= n_ptiles) {
             const int tt = t - n_ptiles;
 #pragma unroll
@@ -282,7 +276,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     };
 
     // row maximum of a block (both lane halves), -inf for a fully masked row
-    auto block_max = [&](const f32x16 (&S)[2], int qt) {
+    auto block_max = [&](const f32x16 (&S)[2], int qt) __attribute__((always_inline)) {
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[qt][r]);
@@ -291,7 +285,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
 
     // exp2 of one block against the running maximum; adds to the row sums and returns whether
     // any of this lane's block sums left the safe range
-    auto exps = [&](const f32x16 (&S)[2], bf16x8 (&P)[2][2]) {
+    auto exps = [&](const f32x16 (&S)[2], bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
         bool bad = false;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
@@ -313,7 +307,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
 
     // fast path: the reference maximum of a row is set once, by the first block in which the
     // row sees a key; afterwards the accumulators are never rescaled
-    auto seed_max = [&](const f32x16 (&S)[2]) {
+    auto seed_max = [&](const f32x16 (&S)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             const float mx = block_max(S, qt);
@@ -322,7 +316,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     };
 
     // exact path: move the running maximum to cover the block and rescale what is accumulated
-    auto exact_max = [&](const f32x16 (&S)[2]) {
+    auto exact_max = [&](const f32x16 (&S)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             const float m_new = fmaxf(m_run[qt], block_max(S, qt));
@@ -340,39 +334,78 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
         }
     };
 
-    // one pass over every tile of the part; EXACT selects the rescaling path
-    auto run_pass = [&](auto exact_tag) -> bool {
+    // Barrier that orders LDS only: outstanding global loads (the prefetched tiles) stay in
+    // flight across it, unlike a full __syncthreads().
+    auto lds_barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+
+    // compute one tile from LDS stage s
+    auto compute_tile = [&](int t, int s, auto exact_tag) __attribute__((always_inline)) -> bool {
         constexpr bool EXACT = decltype(exact_tag)::value;
         bool bad = false;
-        if (n_tiles > 0) {
-            load_tile(0);
-            store_tile(0);
-        }
-        __syncthreads();
-        for (int t = 0; t < n_tiles; ++t) {
-            const int s = t & 1;
-            if (t + 1 < n_tiles) load_tile(t + 1);
-            if (wave_active) {
-                const uint16_t *Ks = smem + s * STAGE;
-                const uint16_t *Vs = Ks + TILE;
-                const bool seed = t == 0 || t >= n_ptiles;
-                f32x16 S0[2], S1[2];
-                bf16x8 P0[2][2], P1[2][2];
-                qk(Ks, 0, S0);
-                mask_block(S0, t, 0);
-                qk(Ks, 1, S1);  // overlaps the exponentials of block 0
-                if (EXACT) exact_max(S0);
-                else if (seed) seed_max(S0);
-                bad |= exps(S0, P0);
-                mask_block(S1, t, 1);
-                pv(Vs, 0, P0);  // overlaps the exponentials of block 1
-                if (EXACT) exact_max(S1);
-                else if (seed) seed_max(S1);
-                bad |= exps(S1, P1);
-                pv(Vs, 1, P1);
+        if (!wave_active) return false;
+        const uint16_t *Ks = smem + s * STAGE;
+        const uint16_t *Vs = Ks + TILE;
+        const bool seed = t == 0 || t >= n_ptiles;
+        f32x16 S0[2], S1[2];
+        bf16x8 P0[2][2], P1[2][2];
+        qk(Ks, 0, S0);
+        mask_block(S0, t, 0);
+        qk(Ks, 1, S1);  // overlaps the exponentials of block 0
+        if (EXACT) exact_max(S0);
+        else if (seed) seed_max(S0);
+        bad |= exps(S0, P0);
+        mask_block(S1, t, 1);
+        pv(Vs, 0, P0);  // overlaps the exponentials of block 1
+        if (EXACT) exact_max(S1);
+        else if (seed) seed_max(S1);
+        bad |= exps(S1, P1);
+        pv(Vs, 1, P1);
+        return bad;
+    };
+
+    // One pass over every tile of the part; EXACT selects the rescaling path. With four
+    // wavefronts, tiles are loaded two ahead into alternating register sets (A, B) and written to
+    // alternating LDS stages, so two tiles' worth of loads are in flight while one is computed;
+    // smaller workgroups (more chunks per thread) load one tile ahead.
+    auto run_pass = [&](auto exact_tag) __attribute__((always_inline)) -> bool {
+        bool bad = false;
+        if constexpr (NW == 4) {
+            if (n_tiles > 0) {
+                load_tile(0, stA_K, stA_V);
+                store_tile(0, stA_K, stA_V);
             }
-            if (t + 1 < n_tiles) store_tile(s ^ 1);
-            __syncthreads();
+            if (n_tiles > 1) load_tile(1, stB_K, stB_V);
+            lds_barrier();
+            for (int t = 0; t < n_tiles; t += 2) {
+                // tile t in stage 0; set B holds tile t + 1
+                if (t + 2 < n_tiles) load_tile(t + 2, stA_K, stA_V);
+                bad |= compute_tile(t, 0, exact_tag);
+                if (t + 1 < n_tiles) store_tile(1, stB_K, stB_V);
+                lds_barrier();
+                if (t + 1 >= n_tiles) break;
+                // tile t + 1 in stage 1; set A holds tile t + 2
+                if (t + 3 < n_tiles) load_tile(t + 3, stB_K, stB_V);
+                bad |= compute_tile(t + 1, 1, exact_tag);
+                if (t + 2 < n_tiles) store_tile(0, stA_K, stA_V);
+                lds_barrier();
+            }
+        } else {
+            if (n_tiles > 0) {
+                load_tile(0, stA_K, stA_V);
+                store_tile(0, stA_K, stA_V);
+            }
+            lds_barrier();
+            for (int t = 0; t < n_tiles; ++t) {
+                const int s = t & 1;
+                if (t + 1 < n_tiles) load_tile(t + 1, stA_K, stA_V);
+                bad |= compute_tile(t, s, exact_tag);
+                if (t + 1 < n_tiles) store_tile(s ^ 1, stA_K, stA_V);
+                lds_barrier();
+            }
         }
         return bad;
     };
