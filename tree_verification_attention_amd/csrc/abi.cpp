@@ -75,9 +75,10 @@ int check_prefix(const ta_problem *p) {
     }
     if (!p->k_cache || !p->v_cache || !aligned16(p->k_cache) || !aligned16(p->v_cache))
         return TA_EINVAL;
-    // the kernels address rows with 32-bit offsets from a per-(sequence, head) base
+    // the kernels address a sequence's rows with 32-bit byte offsets from a per-(sequence, head)
+    // base
     const int64_t rows = p->block_table ? p->page_size : p->Lmax;
-    if (rows * p->kv_s1 + p->D > INT32_MAX) return TA_EINVAL;
+    if ((rows * p->kv_s1 + p->D) * es > INT32_MAX) return TA_EINVAL;
     if (p->block_table && p->kv_s0 > INT32_MAX) return TA_EINVAL;
     return TA_OK;
 }
@@ -89,7 +90,7 @@ int check_tree(const ta_problem *p) {
     if (!aligned16(p->k_tree) || !aligned16(p->v_tree)) return TA_EINVAL;
     if (!stride_ok(p->kt_sb, es) || !stride_ok(p->kt_st, es) || !stride_ok(p->kt_sh, es))
         return TA_EINVAL;
-    if ((int64_t)p->T * p->kt_st + p->D > INT32_MAX) return TA_EINVAL;
+    if (((int64_t)p->T * p->kt_st + p->D) * es > INT32_MAX) return TA_EINVAL;
     return TA_OK;
 }
 
@@ -108,10 +109,11 @@ Plan make_plan(const ta_problem *p) {
     pl.rows = (int64_t)p->B * p->T * p->Hq;
     int64_t wg_per_split;
     if (p->dtype == TA_BF16) {
-        const int rb_rows = 4 * ta::kRowsPerWave;
+        // workgroups of 2, 4 or 8 wavefronts, 32 packed rows each
+        const int rb_rows = 8 * ta::kRowsPerWave;
         pl.n_rb = (R + rb_rows - 1) / rb_rows;
         const int nw = (R + ta::kRowsPerWave * pl.n_rb - 1) / (ta::kRowsPerWave * pl.n_rb);
-        pl.nw = nw <= 1 ? 1 : nw <= 2 ? 2 : 4;
+        pl.nw = nw <= 2 ? 2 : nw <= 4 ? 4 : 8;
         wg_per_split = (int64_t)p->B * p->Hkv * pl.n_rb;
     } else {
         wg_per_split = pl.rows;
@@ -126,6 +128,11 @@ Plan make_plan(const ta_problem *p) {
     }
     int64_t chunk = pl.capacity > 0 ? ((int64_t)pl.capacity + n - 1) / n : 1;
     chunk = (chunk + ta::kKeyTile - 1) / ta::kKeyTile * ta::kKeyTile;
+    if (p->block_table && p->dtype == TA_BF16) {
+        // a part's block-table entries are cached in LDS (kPageCache of them)
+        const int64_t most = (int64_t)(ta::kPageCache - 2) * p->page_size;
+        if (chunk > most) chunk = most / ta::kKeyTile * ta::kKeyTile;
+    }
     pl.chunk = (int)chunk;
     pl.n_splits = pl.capacity > 0 ? (int)((pl.capacity + chunk - 1) / chunk) : 1;
     const int64_t parts = pl.n_splits;

@@ -9,7 +9,9 @@ namespace ta {
 // Keys per LDS tile of the bf16 attention kernel (two 32-key MFMA sub-tiles).
 constexpr int kKeyTile = 64;
 // Packed query rows (tree node x GQA group member) handled by one wavefront.
-constexpr int kRowsPerWave = 64;
+constexpr int kRowsPerWave = 32;
+// Block-table entries of one part that the bf16 kernel caches in LDS (paged layout).
+constexpr int kPageCache = 2048;
 
 // Device-side view of one attention launch. Part p (0 <= p < n_splits) covers prefix keys
 // [p * chunk, min((p + 1) * chunk, seq_len)) when with_prefix is set, and the last part also
