@@ -37,6 +37,7 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 KERNEL_NAME = "attn_bf16_kernel"
 COPY_BYTES = 1 << 30
+FLUSH_BYTES = 1 << 29
 CSRC = os.path.join(ROOT, "tree_verification_attention_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -137,13 +138,16 @@ def time_case(case, steps, warmup, label):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-    # the dominant kernel alone, same stream, same events
+    # the dominant kernel alone, same stream, same events; before each launch a 512 MiB fill
+    # (outside the events) evicts the 256 MB last-level cache and the L2s
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     for _ in range(warmup):
         part()
     torch.cuda.synchronize()
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for i in range(steps):
+        flush.zero_()
         kev[i][0].record(stream)
         part()
         kev[i][1].record(stream)
@@ -163,38 +167,50 @@ def pct(xs, q):
     return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
 
 
-def cpu_baseline(case, threads):
-    """The oracle on a bounded sample: every node and head of sequence 0."""
+def cpu_baseline(case, threads, budget_s=10.0):
+    """The oracle on a bounded sample: whole sequences (every node and head over its prefix and
+    tree), one after another, until about ``budget_s`` seconds of CPU work are done."""
     import numpy as np
 
     import oracle
 
     wl = case.wl
-    rows = np.array([(0, i, h) for i in range(wl.T) for h in range(wl.Hq)], dtype=np.int32)
-    print(f"[bench] cpu baseline: {len(rows)} rows on {threads} threads", file=sys.stderr,
-          flush=True)
-    t0 = time.perf_counter()
-    oracle.attend_case(case, rows=rows, nthreads=threads)
-    dt = time.perf_counter() - t0
     es = 2 if wl.dtype == "bf16" else 4
-    L0 = int(case.seq_lens[0])
-    sample_bytes = (2 * es * wl.Hkv * wl.D * L0 + es * wl.T * wl.Hq * wl.D
-                    + 2 * es * wl.T * wl.Hkv * wl.D + 4 * wl.T + es * wl.T * wl.Hq * wl.D
-                    + 4 * wl.T * wl.Hq)
-    return {"value": sample_bytes / dt / 1e12, "unit": "TB/s", "cores": threads,
+    done_bytes, dt, seqs, rows_done = 0, 0.0, 0, 0
+    for b in range(wl.B):
+        rows = np.array([(b, i, h) for i in range(wl.T) for h in range(wl.Hq)], dtype=np.int32)
+        print(f"[bench] cpu baseline: sequence {b}, {len(rows)} rows on {threads} threads",
+              file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        oracle.attend_case(case, rows=rows, nthreads=threads)
+        dt += time.perf_counter() - t0
+        L = int(case.seq_lens[b])
+        done_bytes += (2 * es * wl.Hkv * wl.D * L + es * wl.T * wl.Hq * wl.D
+                       + 2 * es * wl.T * wl.Hkv * wl.D + 4 * wl.T + es * wl.T * wl.Hq * wl.D
+                       + 4 * wl.T * wl.Hq)
+        seqs += 1
+        rows_done += len(rows)
+        if dt >= budget_s:
+            break
+    lens = [int(x) for x in case.seq_lens[:seqs]]
+    return {"value": done_bytes / dt / 1e12, "unit": "TB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"sequence 0 of {wl.B}: all {wl.T} nodes x {wl.Hq} q-heads over its "
-                      f"{L0}-token prefix and tree ({len(rows)} rows), fp64 two-pass softmax",
+            "sample": f"sequences 0..{seqs - 1} of {wl.B} (prefix lengths {lens}): every node x "
+                      f"q-head over its prefix and tree ({rows_done} rows), fp64 two-pass softmax",
             "seconds": round(dt, 3),
-            "us_per_layer_extrapolated": round(dt * 1e6 * int(case.seq_lens.sum()) / max(L0, 1), 1)}
+            "us_per_layer_extrapolated": round(dt * 1e6 * int(case.seq_lens.sum()) / max(sum(lens), 1), 1)}
+
+
+def traffic_path(workload):
+    return os.path.join(PROFILES, f"{KERNEL_NAME}_{workload}_traffic.txt")
 
 
 def traffic_entry(workload):
-    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        t = json.load(f)
+        t = json.loads("".join(ln for ln in f if not ln.startswith("#")))
     if t.get("kernel_src_sha256") != kernel_source_hash():
         return None   # the kernel changed since the counters were taken
     return t
@@ -215,45 +231,106 @@ def parse_pmc(fetch_dir, write_dir, workload):
     what the counters read for a plain copy of known size."""
 
     def read(d, counter):
-        vals = {}
+        out = []   # (kernel name, value) per dispatch
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(path) as f:
                 for row in csv.DictReader(f):
-                    if row.get("Counter_Name") != counter:
-                        continue
-                    name = row["Kernel_Name"]
-                    vals.setdefault(name, []).append(float(row["Counter_Value"]))
-        return vals
+                    if row.get("Counter_Name") == counter:
+                        out.append((row["Kernel_Name"], float(row["Counter_Value"])))
+        return out
 
-    def pick(vals, needle):
-        keys = [k for k in vals if needle in k]
-        if not keys:
-            raise SystemExit(f"no dispatches of {needle} in counters: {list(vals)[:8]}")
-        xs = [v for k in keys for v in vals[k]]
-        return statistics.mean(xs), len(xs), keys[0]
+    def kernel(vals):
+        xs = [v for k, v in vals if KERNEL_NAME in k]
+        if not xs:
+            raise SystemExit(f"no dispatches of {KERNEL_NAME} in the counters")
+        return statistics.mean(xs), len(xs), next(k for k, _ in vals if KERNEL_NAME in k)
+
+    def copy(vals):
+        # the 1 GiB calibration copies: the largest copy dispatches (input uploads are tiny)
+        xs = [(k, v) for k, v in vals if "copy" in k.lower()]
+        if not xs:
+            raise SystemExit("no copy dispatches in the counters (run with --copy-calibration)")
+        top = max(v for _, v in xs)
+        big = [v for _, v in xs if v >= 0.9 * top]
+        return statistics.mean(big), len(big), xs[0][0]
 
     fetch = read(fetch_dir, "FETCH_SIZE")
     write = read(write_dir, "WRITE_SIZE")
-    kf, nkf, kname = pick(fetch, KERNEL_NAME)
-    kw, _, _ = pick(write, KERNEL_NAME)
-    # the plain copy: the dispatch whose name mentions copy and whose fetch is largest
-    copies = {k: v for k, v in fetch.items() if "copy" in k.lower() or "elementwise" in k.lower()}
-    cname = max(copies, key=lambda k: statistics.mean(copies[k]))
-    cf = statistics.mean(fetch[cname])
-    cw = statistics.mean(write.get(cname, [0.0]))
+    kf, nkf, kname = kernel(fetch)
+    kw, _, _ = kernel(write)
+    cf, ncf, cname = copy(fetch)
+    cw, _, _ = copy(write)
     f_scale = COPY_BYTES / (cf * 1024.0)
-    w_scale = COPY_BYTES / (cw * 1024.0) if cw else float("nan")
+    w_scale = COPY_BYTES / (cw * 1024.0)
     entry = {"workload": workload, "kernel": kname, "dispatches": nkf,
-             "fetch_kib": kf, "write_kib": kw, "copy_kernel": cname, "copy_fetch_kib": cf,
+             "fetch_kib": kf, "write_kib": kw, "copy_kernel": cname, "copy_dispatches": ncf, "copy_fetch_kib": cf,
              "copy_write_kib": cw, "fetch_scale": f_scale, "write_scale": w_scale,
              "fetch_bytes": kf * 1024.0 * f_scale, "write_bytes": kw * 1024.0 * w_scale,
              "kernel_src_sha256": kernel_source_hash()}
     entry["traffic_bytes"] = entry["fetch_bytes"] + entry["write_bytes"]
     os.makedirs(PROFILES, exist_ok=True)
-    out = os.path.join(PROFILES, f"traffic_{workload}.json")
+    out = traffic_path(workload)
+    run = (f"python3 bench.py --workload {workload} --steps 4 --warmup 1 --no-secondary "
+           f"--no-cpu-baseline --copy-calibration")
     with open(out, "w") as f:
+        f.write(f"# HBM traffic of {kname} on workload {workload}, per dispatch.\n"
+                f"# FETCH pass: rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- {run}\n"
+                f"# WRITE pass: rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR -o run --output-format csv -- {run}\n"
+                f"# summary:    python3 bench.py --workload {workload} --parse-pmc FETCH_DIR WRITE_DIR\n"
+                f"# Counter KiB are scaled by bytes / KiB-read of the plain 1 GiB copy in the same runs.\n")
         json.dump(entry, f, indent=1)
+        f.write("\n")
     print(json.dumps(entry, indent=1))
+
+
+def stats_summary(stats_dir, workload, steps):
+    """Text summary of a rocprofv3 --kernel-trace --stats run of this script."""
+    import re
+
+    def one(pattern):
+        paths = glob.glob(os.path.join(stats_dir, "**", pattern), recursive=True)
+        if not paths:
+            raise SystemExit(f"no {pattern} under {stats_dir}")
+        return paths[0]
+
+    with open(one("*kernel_stats.csv")) as f:
+        stats = list(csv.DictReader(f))
+    with open(one("*kernel_trace.csv")) as f:
+        trace = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            for r in trace if KERNEL_NAME in r["Kernel_Name"]]
+    alone = durs[-steps:]            # the kernel-alone loop: the last `steps` launches
+    fused = durs[:-steps][-steps:]   # the timed fused loop before it
+    bench_avg = None
+    logs = glob.glob(os.path.join(os.path.dirname(stats_dir.rstrip("/")),
+                                  os.path.basename(stats_dir.rstrip("/")) + ".log"))
+    if logs:
+        m = re.search(r'"kernel_avg_us": ([0-9.]+)', open(logs[0]).read())
+        bench_avg = float(m.group(1)) if m else None
+    out = os.path.join(PROFILES, f"{KERNEL_NAME}_{workload}_stats.txt")
+    lines = [
+        f"# rocprofv3 kernel statistics, workload {workload}",
+        f"# command: rocprofv3 --kernel-trace --stats -d STATS_DIR -o run --output-format csv -- "
+        f"python3 bench.py --workload {workload} --steps {steps} --warmup 5 --no-secondary "
+        f"--no-cpu-baseline",
+        f"# summary: python3 bench.py --workload {workload} --steps {steps} --stats-summary STATS_DIR",
+        "",
+        "kernel | calls | average us | min us | max us",
+    ]
+    for r in stats:
+        lines.append(f"{r['Name'][:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f}")
+    lines += [
+        "",
+        f"{KERNEL_NAME}, timed fused-forward loop ({len(fused)} launches, no cache flush): "
+        f"average {statistics.mean(fused):.2f} us",
+        f"{KERNEL_NAME}, kernel-alone loop ({len(alone)} launches, 512 MiB flush before each): "
+        f"average {statistics.mean(alone):.2f} us, median {statistics.median(alone):.2f} us",
+        f"bench.py kernel_avg_us (HIP events around the same kernel-alone launches): {bench_avg}",
+    ]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -269,7 +346,13 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB copies (reference for HBM counters)")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--stats-summary", metavar="STATS_DIR",
+                    help="write the text summary of a rocprofv3 --kernel-trace --stats run")
     args = ap.parse_args()
+
+    if args.stats_summary:
+        stats_summary(args.stats_summary, args.workload, args.steps)
+        return
 
     if args.parse_pmc:
         parse_pmc(args.parse_pmc[0], args.parse_pmc[1], args.workload)
