@@ -180,6 +180,26 @@ def test_device_errors_set_the_flag():
     assert err & _lib.TA_DEV_BAD_PARENT and err & _lib.TA_DEV_BAD_LEN
 
 
+@pytest.mark.parametrize("splits", [1, 2, 0])
+def test_rising_logits_take_the_exact_path(splits):
+    """Prefix keys from position 256 on are shifted by +48 in every channel, so a row whose query
+    sums to more than about one standard deviation scores them ~48 nats above the first tile: their
+    exponentials against the first tile's maximum overflow fp32, and only the exact (moving
+    maximum) path gives a finite, correct result."""
+    w = wl(B=2, Hq=8, Hkv=2, T=16, L=(600, 900))
+    case = inputs.make_case(w, 7)
+    k = inputs.bf16_bits_to_f32(case.k_cache)
+    for b, L in enumerate(case.seq_lens):
+        k[b, 256:L] += 48.0
+    case.k_cache[...] = inputs.f32_to_bf16_bits(k)
+    say(f"rising logits, splits={splits}, lens={case.seq_lens.tolist()}")
+    o, lse, err = run_forward(case, num_splits=splits)
+    assert err == 0
+    o_ref, lse_ref = oracle.attend_case(case)
+    assert np.max(lse_ref) > 40.0   # the shifted keys dominate some rows
+    check(case, o, lse, o_ref, lse_ref, f"rising logits splits={splits}")
+
+
 def test_determinism():
     case = inputs.make_case(wl(L=(900, 1500)), 5)
     o1, l1, _ = run_forward(case)
@@ -203,8 +223,8 @@ def sample_rows(case, n_per_b=12, seed=0):
     return np.array(rows, dtype=np.int32)
 
 
-FULL = ["mha_7b", "gqa_64k", "gqa_64k_pinned", "sweep_t1", "sweep_t6", "sweep_t16", "sweep_t128",
-        "long_reasoning", "gqa_64k_beam"]
+FULL = ["mha_7b", "gqa_64k", "gqa_64k_pinned", "sweep_t1", "sweep_t6", "sweep_t16", "sweep_t32",
+        "sweep_t64", "sweep_t128", "long_reasoning", "gqa_64k_beam"]
 
 
 @pytest.mark.parametrize("name", FULL)
