@@ -9,34 +9,36 @@
 //
 // Query packing. The G = Hq / Hkv query heads that share a KV head and the T tree nodes form
 // R = T * G packed rows, row r = node * G + group member. Each wavefront owns 32 rows (one
-// 32-column MFMA tile, ~200 registers, so two wavefronts share every SIMD and the hardware
-// interleaves one's MFMAs with the other's softmax); a workgroup of NW wavefronts shares every
-// K/V tile, so the KV stream is read from HBM once per 32 * NW rows.
+// 32-column MFMA tile, so two wavefronts share every SIMD and the hardware interleaves one's
+// MFMAs with the other's softmax); a workgroup of NW wavefronts shares every K/V tile, so the KV
+// stream is read from HBM once per 32 * NW rows.
 //
-// Per 64-key tile:
-//   HBM -> registers: 16-byte buffer loads whose per-lane offsets never change; the tile's
-//     position is a scalar offset, and rows past the end of the sequence read as zeros. The next
-//     tile's loads are in flight during the current tile's MFMAs; registers -> LDS (two stages),
-//     ordered by an LDS-only barrier.
-//   K keeps its [key][d] layout; V is transposed on the way into LDS, to [d][key] with keys
-//     permuted inside each 16-key group so that one lane's eight PV k-slots are one contiguous
-//     16-byte read. Both rows are padded by 16 bytes, which spreads the 16 lanes of every read
-//     and write phase over distinct banks and keeps every operand address a single per-lane base
-//     plus an immediate.
-//   S^T = K Q^T on v_mfma_f32_32x32x16_bf16, 32 keys at a time: the keys are the MFMA rows, so
-//     every lane holds scores of a single query row -- the layout P^T needs as a B operand. All
-//     operand reads of a 32-key block are issued before its MFMA chain.
-//   O^T += V^T P^T on the same MFMA.
-//   Softmax in fp32 with exp2 (log2(e) folded into the scale). The first tile and the tree tiles
-//     take an exact path that moves each row's maximum and rescales what is accumulated; the
-//     remaining prefix tiles keep the maximum fixed and never rescale (no per-element maximum,
-//     no accumulator traffic). Should a block's exponentials there sum past 2^64 the whole
-//     workgroup redoes its part on the exact path.
+// KV streaming. 64-key tiles of K and V go from HBM straight into LDS with direct-to-LDS loads
+// (each instruction moves 16 bytes per lane into 1 KB of consecutive LDS), through a ring of NS
+// stages: while a tile is computed, the next NS - 1 tiles are in flight, with no registers held
+// for them. The loads are issued from inline assembly and their completion is awaited with
+// explicit vector-memory counter waits, one tile at a time; the compiler would otherwise wait
+// for every outstanding LDS load before any LDS read.
+//
+// LDS layouts (16-byte chunk = 8 bf16 of one key row):
+//   K: blocks of 16 keys x 4 chunks, chunk-major inside the block. One load instruction fills
+//      one block from 16 rows x 64 contiguous bytes; the QK operand read of 16 lanes (16
+//      consecutive keys, one chunk) is 256 consecutive bytes.
+//   V: blocks of 4 keys x 4 chunks, key-major inside the block. One load instruction fills four
+//      blocks from 4 whole key rows. The PV operand V^T comes from the transposing LDS read
+//      (ds_read_b64_tr_b16): 16 lanes that each address 4 d-values of one key return to every
+//      lane 4 keys of one d; the 32 lanes of a half-wave touch one block's 16 chunks once each.
+//   Every operand address is one per-lane base plus an immediate.
+//
+// Per 32-key block: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys are the MFMA rows, so every
+// lane holds scores of a single query row -- the layout P^T needs as a B operand), softmax in
+// fp32 with exp2 (log2(e) folded into the scale), O^T += V^T P^T on the same MFMA. The first tile
+// and the tree tiles take an exact path that moves each row's maximum and rescales what is
+// accumulated; the remaining prefix tiles keep the maximum fixed and never rescale. Should a
+// block's exponentials there sum past 2^64 the whole workgroup redoes its part on the exact path.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
-
-#include <type_traits>
 
 #include "ancestors.h"
 #include "launch.h"
@@ -45,8 +47,10 @@
 namespace ta {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // A 32-key block whose exponentials (relative to the fixed maximum) sum past this sends the
 // workgroup to the exact path; below it nothing can overflow fp32 or bf16.
@@ -54,29 +58,51 @@ constexpr float kSumGuard = 18446744073709551616.0f;  // 2^64
 
 #define TA_INLINE __attribute__((always_inline))
 
+// Wait until at most N vector-memory operations of this wavefront are outstanding.
+template <int N>
+__device__ TA_INLINE void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// LDS byte address of a shared-memory pointer (the value a load-to-LDS instruction takes in M0).
+__device__ TA_INLINE uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// 16 bytes per lane from saddr + voff into LDS at m0 + 16 * lane. The compiler does not insert
+// wait states for what an inline-assembly load reads, so the s_nop supplies them: five after a
+// VALU write of an SGPR the load reads (saddr may come from v_readfirstlane), one after an SALU
+// write of M0.
+__device__ TA_INLINE void load_lds_saddr(const void *saddr, uint32_t voff, uint32_t m0) {
+    const uint64_t p = (uint64_t)(uintptr_t)saddr;
+    const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p) |
+                       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32);
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(u), "{m0}"(m0) : "memory");
+}
+
 template <int D, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     constexpr int KT = kKeyTile;
     constexpr int NT = NW * 64;
-    constexpr int DCH = D / 8;                      // 16-byte chunks per key row
-    constexpr int KN = KT * DCH / NT;               // K chunks per thread per tile
-    constexpr int VITEMS = (KT / 2) * DCH;          // (key pair, chunk) items of a V tile
-    constexpr int VN = (VITEMS + NT - 1) / NT;      // V items per thread per tile
-    constexpr int KS = D / 16;                      // MFMA k-steps over the head dimension
-    constexpr int DT = D / 32;                      // 32-row tiles of O^T
-    constexpr int KROW = D + 8;                     // padded K row (bf16 elements)
-    constexpr int VROW = KT + 8;                    // padded V^T row (bf16 elements)
-    constexpr int KTILE = KT * KROW;
-    constexpr int STAGE = KTILE + D * VROW;         // bf16 elements of one LDS stage
-    constexpr bool DEEP = false;                    // two tiles of loads in flight
-    static_assert((KT * DCH) % NT == 0, "K chunks must divide over the threads");
-    static_assert(sizeof(AncestorLds) <= 2 * STAGE * 2, "mask scratch must fit the tile LDS");
+    constexpr int DCH = D / 8;                  // 16-byte chunks per key row
+    constexpr int CB = DCH / 4;                 // 4-chunk column blocks per key row
+    constexpr int KS = D / 16;                  // MFMA k-steps over the head dimension
+    constexpr int DT = D / 32;                  // 32-row tiles of O^T
+    constexpr int NS = 4;                       // LDS stages in the ring
+    constexpr int TILE_B = KT * D * 2;          // bytes of one K (or V) tile
+    constexpr int STAGE_B = 2 * TILE_B;
+    constexpr int NI = KT * DCH / 64;           // load instructions per K (or V) tile
+    constexpr int NIW = 2 * NI / NW;            // load instructions per wavefront per tile
+    static_assert((2 * NI) % NW == 0, "tile loads must divide over the wavefronts");
+    static_assert(sizeof(AncestorLds) <= NS * STAGE_B, "mask scratch must fit the tile LDS");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE_B];
     __shared__ uint64_t node_mask[TA_MAX_TREE][kMaskWords];
     __shared__ int32_t page_cache[PAGED ? kPageCache : 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hf = lane >> 5, l32 = lane & 31;
     const int part = blockIdx.x;
     const int g = blockIdx.y / a.n_rb, rb = blockIdx.y % a.n_rb;
@@ -144,12 +170,30 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     }
     __syncthreads();  // page cache and masks visible; the tile stages reuse the mask scratch
 
-    // ---- KV tile staging: HBM -> registers -> LDS.
-    // K: thread t moves chunk (t % DCH) of key rows t / DCH + i * NT / DCH.
-    // V: item i = t + n * NT is key pair (i % 32) at chunk (i / 32): keys 2*(i%32) and +1.
-    // Contiguous prefix and tree tiles use buffer loads: a row past the end of the sequence (or
-    // tree) reads as zeros, and rows past the end of the part are masked to -inf; the paged
-    // prefix clamps its rows to the part's last row instead.
+    // ---- this lane's share of a tile's loads: instruction i of this wavefront is tile-load
+    // number j = wave * NIW + i; j < NI fills K block j, otherwise V blocks 4 (j - NI) .. + 3.
+    // ld_row / ld_off: key row inside the tile and byte offset inside the row; ld_lds: LDS byte
+    // offset of the instruction's 1 KB inside a stage.
+    int ld_row[NIW];
+    uint32_t ld_off[NIW], ld_lds[NIW];
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+        const int j = wave * NIW + i;
+        if (j < NI) {
+            const int ri = j / CB, ci = j % CB;
+            ld_row[i] = 16 * ri + (lane & 15);
+            ld_off[i] = 16u * (uint32_t)(4 * ci + (lane >> 4));
+            ld_lds[i] = 1024u * (uint32_t)j;
+        } else {
+            const int jv = j - NI;
+            const int blk = 4 * jv + (lane >> 4);
+            const int ka = blk / CB, cb = blk % CB;
+            ld_row[i] = 4 * ka + ((lane >> 2) & 3);
+            ld_off[i] = 16u * (uint32_t)(4 * cb + (lane & 3));
+            ld_lds[i] = (uint32_t)TILE_B + 1024u * (uint32_t)jv;
+        }
+    }
+    const uint32_t smem_lds = lds_addr(smem);
     const uint32_t prow = 2u * (uint32_t)a.kv_s1, trow = 2u * (uint32_t)a.kt_st;
     const uint64_t ppage = 2ull * (uint64_t)a.kv_s0;
     const char *kc_b = reinterpret_cast<const char *>(a.kc) +
@@ -158,94 +202,51 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
                        2 * ((PAGED ? 0 : b * a.kv_s0) + g * a.kv_s2);
     const char *kt_b = reinterpret_cast<const char *>(a.kt) + 2 * (b * a.kt_sb + g * a.kt_sh);
     const char *vt_b = reinterpret_cast<const char *>(a.vt) + 2 * (b * a.kt_sb + g * a.kt_sh);
-    const int seq_len = a.with_prefix ? min(max(a.seq_lens[b], 0), a.capacity) : 0;
-    const __amdgpu_buffer_rsrc_t rs_kc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)kc_b, (short)0, PAGED ? 0 : seq_len * (int)prow, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs_vc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)vc_b, (short)0, PAGED ? 0 : seq_len * (int)prow, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs_kt = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)kt_b, (short)0, has_tree ? a.T * (int)trow : 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs_vt = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)vt_b, (short)0, has_tree ? a.T * (int)trow : 0, 0x00020000);
 
-    u32x4 stA_K[KN], stA_V[2 * VN];
-    u32x4 stB_K[DEEP ? KN : 1], stB_V[DEEP ? 2 * VN : 1];
-
-    auto load_tile = [&](int t, u32x4 (&sK)[KN], u32x4 (&sV)[2 * VN]) TA_INLINE {
+    // Issue tile t's loads into stage t % NS. Rows past the end of the part (or of the tree) are
+    // clamped to its last row: they are masked out of the scores, and a clamped row holds finite
+    // values, so 0 * V stays 0.
+    auto issue_tile = [&](int t) TA_INLINE {
+        const uint32_t st = smem_lds + (uint32_t)((t % NS) * STAGE_B);
         const bool tree_tile = t >= n_ptiles;
         if (tree_tile || !PAGED) {
             const int k0 = tree_tile ? (t - n_ptiles) * KT : pb + t * KT;
+            const int last = (tree_tile ? a.T : pe) - 1 - k0;
             const uint32_t rowb = tree_tile ? trow : prow;
-            const __amdgpu_buffer_rsrc_t rk = tree_tile ? rs_kt : rs_kc;
-            const __amdgpu_buffer_rsrc_t rv = tree_tile ? rs_vt : rs_vc;
-            const int soff = k0 * (int)rowb;
+            const char *kb = (tree_tile ? kt_b : kc_b) + (uint64_t)k0 * rowb;
+            const char *vb = (tree_tile ? vt_b : vc_b) + (uint64_t)k0 * rowb;
 #pragma unroll
-            for (int i = 0; i < KN; ++i) {
-                const int c = tid + i * NT;
-                sK[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rk, (int)((c / DCH) * rowb + (c % DCH) * 16u), soff, 0);
-            }
-#pragma unroll
-            for (int n = 0; n < VN; ++n) {
-                const int it = min(tid + n * NT, VITEMS - 1);
-                const int kp = it & 31, dc = it >> 5;
-                sV[2 * n] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rv, (int)((2 * kp) * rowb + dc * 16u), soff, 0);
-                sV[2 * n + 1] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rv, (int)((2 * kp + 1) * rowb + dc * 16u), soff, 0);
+            for (int i = 0; i < NIW; ++i) {
+                const uint32_t off = (uint32_t)min(ld_row[i], last) * rowb + ld_off[i];
+                const bool is_k = wave * NIW + i < NI;  // uniform per wavefront
+                load_lds_saddr(is_k ? kb : vb, off, st + ld_lds[i]);
             }
         } else {
+            // Every instruction's rows form one aligned group of at most 16 keys (K: 16, V: 4
+            // rows at D = 128, 8 at D = 64), and pages hold a power of two >= 16 keys, so an
+            // instruction reads a single page (clamped rows stay inside the group or all land on
+            // the last row): the page base is a scalar and the lanes add 32-bit row offsets.
             const int k0 = pb + t * KT;
             const int last = pe - 1 - k0;
-            auto row_addr = [&](const char *base, int row) TA_INLINE -> const char * {
-                const int key = k0 + min(row, last);
-                const int pg = page_cache[(key >> a.page_shift) - page0];
-                return base + (uint64_t)pg * ppage + (uint32_t)(key & a.page_mask) * prow;
-            };
 #pragma unroll
-            for (int i = 0; i < KN; ++i) {
-                const int c = tid + i * NT;
-                sK[i] = *reinterpret_cast<const u32x4 *>(row_addr(kc_b, c / DCH) + (c % DCH) * 16);
-            }
-#pragma unroll
-            for (int n = 0; n < VN; ++n) {
-                const int it = min(tid + n * NT, VITEMS - 1);
-                const int kp = it & 31, dc = it >> 5;
-                sV[2 * n] = *reinterpret_cast<const u32x4 *>(row_addr(vc_b, 2 * kp) + dc * 16);
-                sV[2 * n + 1] = *reinterpret_cast<const u32x4 *>(row_addr(vc_b, 2 * kp + 1) + dc * 16);
+            for (int i = 0; i < NIW; ++i) {
+                const int j = wave * NIW + i;
+                const int g0 = j < NI ? 16 * (j / CB) : 4 * ((4 * (j - NI)) / CB);  // group's first row
+                const int pkey = k0 + min(g0, last);
+                const int pg = __builtin_amdgcn_readfirstlane(page_cache[(pkey >> a.page_shift) - page0]);
+                const char *base = (j < NI ? kc_b : vc_b) + (uint64_t)pg * ppage;
+                const int key = k0 + min(ld_row[i], last);
+                load_lds_saddr(base, (uint32_t)(key & a.page_mask) * prow + ld_off[i], st + ld_lds[i]);
             }
         }
     };
 
-    // LDS positions. K: row k, chunk c at k * KROW + 8c. V^T: row d, key k at d * VROW +
-    // 8 * (2*(k/16) + (k/4)%2) + 4 * ((k/8)%2) + k%4: the 16-byte block 2*(k/16) + h holds keys
-    // 16*(k/16) + 4h + {0..3} and + 8 + {0..3}, the eight k-slots one PV lane consumes.
-    auto vt_off = [](int d, int k) TA_INLINE {
-        return d * VROW + 8 * (2 * (k >> 4) + ((k >> 2) & 1)) + 4 * ((k >> 3) & 1) + (k & 3);
-    };
-
-    auto store_tile = [&](int s, const u32x4 (&sK)[KN], const u32x4 (&sV)[2 * VN]) TA_INLINE {
-        uint16_t *Ks = smem + s * STAGE;
-        uint16_t *Vs = Ks + KTILE;
-#pragma unroll
-        for (int i = 0; i < KN; ++i) {
-            const int c = tid + i * NT;
-            *reinterpret_cast<u32x4 *>(Ks + (c / DCH) * KROW + (c % DCH) * 8) = sK[i];
-        }
-#pragma unroll
-        for (int n = 0; n < VN; ++n) {
-            const int it = tid + n * NT;
-            if (VITEMS % NT == 0 || it < VITEMS) {
-                const int kp = it & 31, dc = it >> 5;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t w0 = sV[2 * n][e >> 1], w1 = sV[2 * n + 1][e >> 1];
-                    const uint32_t pk = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
-                                                : ((w0 & 0xffffu) | (w1 << 16));
-                    *reinterpret_cast<uint32_t *>(Vs + vt_off(dc * 8 + e, 2 * kp)) = pk;
-                }
-            }
-        }
+    // wait for this wavefront's loads of tile t, given the tiles issued after it
+    auto wait_tile = [&](int t) TA_INLINE {
+        const int after = min(NS - 2, n_tiles - 1 - t);
+        if (after >= 2) wait_vmem<2 * NIW>();
+        else if (after == 1) wait_vmem<NIW>();
+        else wait_vmem<0>();
     };
 
     // ---- accumulators and softmax state
@@ -261,13 +262,22 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     };
     const float c2 = a.scale_log2;
 
+    // Operand read bases (bytes inside a stage). K: lane (l32, hf) reads key jb*32 + l32, chunk
+    // 2*ks + hf. V: lane (g16 = lane / 16, j = lane % 16) addresses key 4*hf + j/4 (+ 16u + 8v of
+    // the block) at d = 16*(g16 % 2) + 4*(j % 4) (+ 32 dt).
+    const uint32_t k_rd = (uint32_t)((l32 >> 4) * CB * 1024 + hf * 256 + (l32 & 15) * 16);
+    const int jv = lane & 15, g16 = lane >> 4;
+    const uint32_t v_rd = (uint32_t)(hf * CB * 256 + (4 * (jv >> 2) + 2 * (g16 & 1) + ((jv & 3) >> 1)) * 16 +
+                                     (jv & 1) * 8);
+
     // S^T for one 32-key block (jb): key jb*32 + 8*(r/4) + 4*hf + r%4 in register r. All K
     // fragments are read before the MFMA chain starts, so the LDS latency is paid once.
-    auto qk = [&](const uint16_t *Ks, int jb, f32x16 &S) TA_INLINE {
+    auto qk = [&](const char *Ks, int jb, f32x16 &S) TA_INLINE {
         bf16x8 kf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            kf[ks] = *reinterpret_cast<const bf16x8 *>(Ks + (jb * 32 + l32) * KROW + (2 * ks + hf) * 8);
+            kf[ks] = *reinterpret_cast<const bf16x8 *>(Ks + k_rd + jb * 2 * CB * 1024 +
+                                                       (ks >> 1) * 1024 + (ks & 1) * 512);
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[r] = 0.f;
 #pragma unroll
@@ -278,14 +288,19 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // V^T fragments of one 32-key block, read ahead of its exponentials
-    auto load_vt = [&](const uint16_t *Vs, int jb, bf16x8 (&vf)[2][DT]) TA_INLINE {
+    // V^T fragments of one 32-key block, read ahead of its exponentials: k-slots 0..3 of a lane
+    // are keys 16u + 4hf + 0..3, k-slots 4..7 the same + 8 (the P^T layout of the S^T tile).
+    auto load_vt = [&](const char *Vs, int jb, bf16x8 (&vf)[2][DT]) TA_INLINE {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                vf[u][dt] = *reinterpret_cast<const bf16x8 *>(
-                    Vs + (dt * 32 + l32) * VROW + 8 * (2 * (2 * jb + u) + hf));
+            for (int dt = 0; dt < DT; ++dt) {
+                const char *p = Vs + v_rd + (8 * jb + 4 * u) * CB * 256 + dt * 256;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+                const bf16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + 2 * CB * 256));
+                vf[u][dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -369,8 +384,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     auto compute_tile = [&](int t, int s, bool cold) TA_INLINE -> bool {
         bool bad = false;
         if (!wave_active) return false;
-        const uint16_t *Ks = smem + s * STAGE;
-        const uint16_t *Vs = Ks + KTILE;
+        const char *Ks = smem + s * STAGE_B;
+        const char *Vs = Ks + TILE_B;
         const bool exact = cold || t == 0 || t >= n_ptiles;
         if (!exact && pb + (t + 1) * KT <= pe) {
             // the hot path: a full prefix tile
@@ -399,45 +414,26 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
         return bad;
     };
 
-    // Barrier that orders LDS only: outstanding global loads (the prefetched tiles) stay in
-    // flight across it, unlike a full __syncthreads().
+    // Barrier that orders LDS only (the loads in flight are tracked by wait_tile).
     auto lds_barrier = []() TA_INLINE {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
 
-    // One pass over every tile of the part. Tile t is staged through LDS stage t % 2; with
-    // eight wavefronts its loads are issued two tiles ahead into register set t % 2.
+    // One pass over every tile of the part. At the top of iteration t the barrier publishes
+    // tile t (every wavefront has waited for its own loads of it) and retires tile t - 1, whose
+    // stage then takes the loads of tile t + NS - 1.
     auto run_pass = [&](bool cold) TA_INLINE -> bool {
         bool bad = false;
-        if (n_tiles > 0) {
-            load_tile(0, stA_K, stA_V);
-            store_tile(0, stA_K, stA_V);
-        }
-        if constexpr (DEEP) {
-            if (n_tiles > 1) load_tile(1, stB_K, stB_V);
+#pragma unroll
+        for (int t = 0; t < NS - 1; ++t)
+            if (t < n_tiles) issue_tile(t);
+        for (int t = 0; t < n_tiles; ++t) {
+            wait_tile(t);
             lds_barrier();
-            for (int t = 0; t < n_tiles; t += 2) {
-                if (t + 2 < n_tiles) load_tile(t + 2, stA_K, stA_V);
-                bad |= compute_tile(t, 0, cold);
-                if (t + 1 < n_tiles) store_tile(1, stB_K, stB_V);
-                lds_barrier();
-                if (t + 1 >= n_tiles) break;
-                if (t + 3 < n_tiles) load_tile(t + 3, stB_K, stB_V);
-                bad |= compute_tile(t + 1, 1, cold);
-                if (t + 2 < n_tiles) store_tile(0, stA_K, stA_V);
-                lds_barrier();
-            }
-        } else {
-            lds_barrier();
-            for (int t = 0; t < n_tiles; ++t) {
-                const int s = t & 1;
-                if (t + 1 < n_tiles) load_tile(t + 1, stA_K, stA_V);
-                bad |= compute_tile(t, s, cold);
-                if (t + 1 < n_tiles) store_tile(s ^ 1, stA_K, stA_V);
-                lds_barrier();
-            }
+            if (t + NS - 1 < n_tiles) issue_tile(t + NS - 1);
+            bad |= compute_tile(t, t % NS, cold);
         }
         return bad;
     };
