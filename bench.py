@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 METRIC = "tree-verify attention µs/layer + achieved HBM TB/s, 64-node tree @64k ctx"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
-KERNEL_NAME = "attn_bf16_kernel"
+KERNEL_NAME = "attn_prefix_kernel"
 COPY_BYTES = 1 << 30
 FLUSH_BYTES = 1 << 29
 CSRC = os.path.join(ROOT, "tree_verification_attention_amd", "csrc")

@@ -17,14 +17,16 @@ constexpr int kAbiVersion = 100;
 // Workgroups the prefix launch aims for per compute unit.
 constexpr int kWgPerCu = 1;
 
+// Workspace parts: parts 0 .. n_splits - 1 hold the prefix splits; part n_splits holds the tree
+// keys and, on the bf16 path, the prefix keys past the last full 64-key tile.
 struct Plan {
-    int nw = 1;        // wavefronts per workgroup (bf16 kernel)
+    int nw = 1;        // wavefronts per workgroup (bf16 kernels)
     int n_rb = 1;      // row blocks per (b, kv-head)
     int n_splits = 1;  // prefix splits
     int chunk = ta::kKeyTile;
     int capacity = 0;  // prefix rows addressable per sequence
     int64_t rows = 0;  // B * T * Hq
-    size_t o_bytes = 0, lse_bytes = 0;  // workspace regions for n_splits parts
+    size_t o_bytes = 0, lse_bytes = 0;  // workspace regions for n_splits + 1 parts
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -135,7 +137,7 @@ Plan make_plan(const ta_problem *p) {
     }
     pl.chunk = (int)chunk;
     pl.n_splits = pl.capacity > 0 ? (int)((pl.capacity + chunk - 1) / chunk) : 1;
-    const int64_t parts = pl.n_splits;
+    const int64_t parts = pl.n_splits + 1;
     pl.o_bytes = align256((size_t)parts * pl.rows * p->D * sizeof(float));
     pl.lse_bytes = align256((size_t)parts * pl.rows * sizeof(float));
     return pl;
@@ -179,9 +181,33 @@ AttnArgs make_args(const ta_problem *p, const Plan &pl, int32_t *err) {
     return a;
 }
 
-int launch_attn(const AttnArgs &a, const Plan &pl, int dtype, hipStream_t s) {
-    const hipError_t e = dtype == TA_BF16 ? ta::launch_attn_bf16(a, pl.nw, s) : ta::launch_attn_f32(a, s);
-    return e == hipSuccess ? TA_OK : TA_EHIP;
+int status(hipError_t e) { return e == hipSuccess ? TA_OK : TA_EHIP; }
+
+// The prefix splits into parts 0 .. n_splits - 1 of (wo, wl) (bf16: full 64-key tiles only).
+int launch_prefix_parts(const ta_problem *p, const Plan &pl, int32_t *err, float *wo, float *wl,
+                        hipStream_t s) {
+    AttnArgs a = make_args(p, pl, err);
+    a.n_splits = pl.n_splits;
+    a.with_prefix = 1;
+    a.out_o = wo;
+    a.out_lse = wl;
+    a.part_so = pl.rows * p->D;
+    a.part_sl = pl.rows;
+    return status(p->dtype == TA_BF16 ? ta::launch_attn_prefix(a, pl.nw, s) : ta::launch_attn_f32(a, s));
+}
+
+// One masked part into (o, l): the tree keys when ``tree`` is set, and on the bf16 path the
+// prefix keys past the last full 64-key tile when ``tail`` is set.
+int launch_last_part(const ta_problem *p, const Plan &pl, int32_t *err, float *o, float *l,
+                     bool tail, bool tree, hipStream_t s) {
+    AttnArgs a = make_args(p, pl, err);
+    a.n_splits = 1;
+    a.with_prefix = tail && p->dtype == TA_BF16;
+    a.tail_only = 1;
+    a.with_tree = tree;
+    a.out_o = o;
+    a.out_lse = l;
+    return status(p->dtype == TA_BF16 ? ta::launch_attn_tree(a, pl.nw, s) : ta::launch_attn_f32(a, s));
 }
 
 }  // namespace
@@ -235,18 +261,19 @@ int tree_attn_prefix(const ta_problem *p, float *o_c, float *lse_c, void *ws, si
     if (!o_c || !lse_c) return TA_EINVAL;
     const Plan pl = make_plan(p);
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
-    AttnArgs a = make_args(p, pl, err_flag);
-    a.n_splits = pl.n_splits;
-    a.with_prefix = 1;
-    a.with_tree = 0;
-    a.out_o = static_cast<float *>(ws);
-    a.out_lse = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
-    a.part_so = pl.rows * p->D;
-    a.part_sl = pl.rows;
-    if ((rc = launch_attn(a, pl, p->dtype, stream))) return rc;
-    MergeArgs m{a.out_o, a.out_lse, a.part_so, a.part_sl, pl.n_splits, nullptr, nullptr,
-                pl.rows, p->D, o_c, lse_c};
-    return ta::launch_merge(m, false, stream) == hipSuccess ? TA_OK : TA_EHIP;
+    float *wo = static_cast<float *>(ws);
+    float *wl = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
+    if ((rc = launch_prefix_parts(p, pl, err_flag, wo, wl, stream))) return rc;
+    int parts = pl.n_splits;
+    if (p->dtype == TA_BF16) {
+        // the prefix keys past the last full tile, as one more part
+        if ((rc = launch_last_part(p, pl, err_flag, wo + pl.n_splits * pl.rows * p->D,
+                                   wl + pl.n_splits * pl.rows, true, false, stream)))
+            return rc;
+        parts += 1;
+    }
+    MergeArgs m{wo, wl, pl.rows * p->D, pl.rows, parts, nullptr, nullptr, pl.rows, p->D, o_c, lse_c};
+    return status(ta::launch_merge(m, false, stream));
 }
 
 int tree_attn_tree(const ta_problem *p, float *o_s, float *lse_s, int32_t *err_flag,
@@ -256,16 +283,8 @@ int tree_attn_tree(const ta_problem *p, float *o_s, float *lse_s, int32_t *err_f
     if (p->B == 0) return TA_OK;
     if ((rc = check_tree(p))) return rc;
     if (!o_s || !lse_s) return TA_EINVAL;
-    Plan pl = make_plan(p);
-    AttnArgs a = make_args(p, pl, err_flag);
-    a.n_splits = 1;
-    a.with_prefix = 0;
-    a.with_tree = 1;
-    a.out_o = o_s;
-    a.out_lse = lse_s;
-    a.part_so = 0;
-    a.part_sl = 0;
-    return launch_attn(a, pl, p->dtype, stream);
+    const Plan pl = make_plan(p);
+    return launch_last_part(p, pl, err_flag, o_s, lse_s, false, true, stream);
 }
 
 int tree_attn_merge(int B, int T, int Hq, int D, const float *o_a, const float *lse_a,
@@ -298,15 +317,11 @@ int tree_attn_partials(const ta_problem *p, void *ws, size_t ws_bytes, int32_t *
     if ((rc = check_prefix(p)) || (rc = check_tree(p))) return rc;
     const Plan pl = make_plan(p);
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
-    AttnArgs a = make_args(p, pl, err_flag);
-    a.n_splits = pl.n_splits;
-    a.with_prefix = 1;
-    a.with_tree = 1;
-    a.out_o = static_cast<float *>(ws);
-    a.out_lse = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
-    a.part_so = pl.rows * p->D;
-    a.part_sl = pl.rows;
-    return launch_attn(a, pl, p->dtype, stream);
+    float *wo = static_cast<float *>(ws);
+    float *wl = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
+    if ((rc = launch_prefix_parts(p, pl, err_flag, wo, wl, stream))) return rc;
+    return launch_last_part(p, pl, err_flag, wo + pl.n_splits * pl.rows * p->D,
+                            wl + pl.n_splits * pl.rows, true, true, stream);
 }
 
 int tree_attn_combine(const ta_problem *p, const void *ws, size_t ws_bytes, void *o, float *lse,
@@ -319,9 +334,9 @@ int tree_attn_combine(const ta_problem *p, const void *ws, size_t ws_bytes, void
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
     const float *wo = static_cast<const float *>(ws);
     const float *wl = reinterpret_cast<const float *>(static_cast<const char *>(ws) + pl.o_bytes);
-    MergeArgs m{wo, wl, pl.rows * p->D, pl.rows, pl.n_splits, nullptr, nullptr,
+    MergeArgs m{wo, wl, pl.rows * p->D, pl.rows, pl.n_splits + 1, nullptr, nullptr,
                 pl.rows, p->D, o, lse};
-    return ta::launch_merge(m, p->dtype == TA_BF16, stream) == hipSuccess ? TA_OK : TA_EHIP;
+    return status(ta::launch_merge(m, p->dtype == TA_BF16, stream));
 }
 
 int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t ws_bytes,

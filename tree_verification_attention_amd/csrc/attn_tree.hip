@@ -1,88 +1,35 @@
-// bf16 split-KV attention kernel for tree verification on gfx950 (CDNA4).
+// bf16 masked attention for tree verification on gfx950 (CDNA4): the speculative part.
 //
-// One workgroup handles one (part, kv-head, row block, sequence). Part p covers one chunk of the
-// committed prefix with no mask; the last part also covers the draft tree's own keys under the
-// ancestor mask. This is the divide step of LongSpec's Hybrid Tree Attention (LongSpec page,
-// "Fast tree attention": the cache part needs no mask, only the few speculative tokens do); the
-// prefix is further divided along its length so that every compute unit streams its own slice,
-// and the parts are combined afterwards by the same log-sum-exp identity (merge kernel).
+// The speculative part of LongSpec's Hybrid Tree Attention: every draft-tree node attends to the
+// tree's own keys under the ancestor mask -- node i sees node j iff j == i or j is an ancestor
+// of i (LongSpec page, "Fast tree attention"; textbook page, tree attention mask). The masks are
+// built per workgroup in LDS from the parent array and applied in-register. The same kernel also
+// takes the prefix keys that the prefix kernel leaves out (those past the last full 64-key tile,
+// in tail mode) and, for direct calls, any prefix chunk: its part covers prefix keys [pb, pe)
+// with no mask, then the tree keys.
 //
-// Query packing. The G = Hq / Hkv query heads that share a KV head and the T tree nodes form
-// R = T * G packed rows, row r = node * G + group member. Each wavefront owns 32 rows (one
-// 32-column MFMA tile, so two wavefronts share every SIMD and the hardware interleaves one's
-// MFMAs with the other's softmax); a workgroup of NW wavefronts shares every K/V tile, so the KV
-// stream is read from HBM once per 32 * NW rows.
+// Layout and streaming are those of the prefix kernel: 32 packed rows (node x GQA group member)
+// per wavefront, 64-key tiles of K and V loaded straight into a ring of LDS stages, K in 16-key
+// x 4-chunk blocks, V in 4-key x 4-chunk blocks read through ds_read_b64_tr_b16, S^T = K Q^T and
+// O^T += V^T P^T on v_mfma_f32_32x32x16_bf16. Rows past the end of the prefix part (or of the
+// tree) are clamped to its last row and masked out of the scores.
 //
-// KV streaming. 64-key tiles of K and V go from HBM straight into LDS with direct-to-LDS loads
-// (each instruction moves 16 bytes per lane into 1 KB of consecutive LDS), through a ring of NS
-// stages: while a tile is computed, the next NS - 1 tiles are in flight, with no registers held
-// for them. The loads are issued from inline assembly and their completion is awaited with
-// explicit vector-memory counter waits, one tile at a time; the compiler would otherwise wait
-// for every outstanding LDS load before any LDS read.
-//
-// LDS layouts (16-byte chunk = 8 bf16 of one key row):
-//   K: blocks of 16 keys x 4 chunks, chunk-major inside the block. One load instruction fills
-//      one block from 16 rows x 64 contiguous bytes; the QK operand read of 16 lanes (16
-//      consecutive keys, one chunk) is 256 consecutive bytes.
-//   V: blocks of 4 keys x 4 chunks, key-major inside the block. One load instruction fills four
-//      blocks from 4 whole key rows. The PV operand V^T comes from the transposing LDS read
-//      (ds_read_b64_tr_b16): 16 lanes that each address 4 d-values of one key return to every
-//      lane 4 keys of one d; the 32 lanes of a half-wave touch one block's 16 chunks once each.
-//   Every operand address is one per-lane base plus an immediate.
-//
-// Per 32-key block: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys are the MFMA rows, so every
-// lane holds scores of a single query row -- the layout P^T needs as a B operand), softmax in
-// fp32 with exp2 (log2(e) folded into the scale), O^T += V^T P^T on the same MFMA. The first tile
-// and the tree tiles take an exact path that moves each row's maximum and rescales what is
-// accumulated; the remaining prefix tiles keep the maximum fixed and never rescale. Should a
-// block's exponentials there sum past 2^64 the whole workgroup redoes its part on the exact path.
+// Softmax: the first tile and the tree tiles take an exact path that moves each row's maximum
+// and rescales what is accumulated; later prefix tiles keep it fixed. Should a block's
+// exponentials there sum past 2^64 the whole workgroup redoes its part on the exact path.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "ancestors.h"
 #include "launch.h"
+#include "lds_dma.h"
 #include "treeattn.h"
 
 namespace ta {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-// A 32-key block whose exponentials (relative to the fixed maximum) sum past this sends the
-// workgroup to the exact path; below it nothing can overflow fp32 or bf16.
-constexpr float kSumGuard = 18446744073709551616.0f;  // 2^64
-
-#define TA_INLINE __attribute__((always_inline))
-
-// Wait until at most N vector-memory operations of this wavefront are outstanding.
-template <int N>
-__device__ TA_INLINE void wait_vmem() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// LDS byte address of a shared-memory pointer (the value a load-to-LDS instruction takes in M0).
-__device__ TA_INLINE uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// 16 bytes per lane from saddr + voff into LDS at m0 + 16 * lane. The compiler does not insert
-// wait states for what an inline-assembly load reads, so the s_nop supplies them: five after a
-// VALU write of an SGPR the load reads (saddr may come from v_readfirstlane), one after an SALU
-// write of M0.
-__device__ TA_INLINE void load_lds_saddr(const void *saddr, uint32_t voff, uint32_t m0) {
-    const uint64_t p = (uint64_t)(uintptr_t)saddr;
-    const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p) |
-                       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32);
-    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(u), "{m0}"(m0) : "memory");
-}
-
 template <int D, int NW, bool PAGED>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) void attn_tree_kernel(AttnArgs a) {
     constexpr int KT = kKeyTile;
     constexpr int NT = NW * 64;
     constexpr int DCH = D / 8;                  // 16-byte chunks per key row
@@ -119,8 +66,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
             if (a.err && tid == 0) atomicOr(a.err, (int32_t)TA_DEV_BAD_LEN);
             L = L < 0 ? 0 : a.capacity;
         }
-        pb = part * a.chunk;
-        pe = min(pb + a.chunk, L);
+        pb = a.tail_only ? (L & ~(KT - 1)) : part * a.chunk;
+        pe = a.tail_only ? L : min(pb + a.chunk, L);
     }
     const int n_ptiles = pe > pb ? (pe - pb + KT - 1) / KT : 0;
     const bool has_tree = a.with_tree && part == a.n_splits - 1;
@@ -179,19 +126,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
         const int j = wave * NIW + i;
-        if (j < NI) {
-            const int ri = j / CB, ci = j % CB;
-            ld_row[i] = 16 * ri + (lane & 15);
-            ld_off[i] = 16u * (uint32_t)(4 * ci + (lane >> 4));
-            ld_lds[i] = 1024u * (uint32_t)j;
-        } else {
-            const int jv = j - NI;
-            const int blk = 4 * jv + (lane >> 4);
-            const int ka = blk / CB, cb = blk % CB;
-            ld_row[i] = 4 * ka + ((lane >> 2) & 3);
-            ld_off[i] = 16u * (uint32_t)(4 * cb + (lane & 3));
-            ld_lds[i] = (uint32_t)TILE_B + 1024u * (uint32_t)jv;
-        }
+        tile_load_pos<DCH>(j >= NI, j < NI ? j : j - NI, lane, ld_row[i], ld_off[i]);
+        ld_lds[i] = j < NI ? 1024u * (uint32_t)j : (uint32_t)TILE_B + 1024u * (uint32_t)(j - NI);
     }
     const uint32_t smem_lds = lds_addr(smem);
     const uint32_t prow = 2u * (uint32_t)a.kv_s1, trow = 2u * (uint32_t)a.kt_st;
@@ -231,7 +167,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < NIW; ++i) {
                 const int j = wave * NIW + i;
-                const int g0 = j < NI ? 16 * (j / CB) : 4 * ((4 * (j - NI)) / CB);  // group's first row
+                const int g0 = tile_load_group<DCH>(j >= NI, j < NI ? j : j - NI);
                 const int pkey = k0 + min(g0, last);
                 const int pg = __builtin_amdgcn_readfirstlane(page_cache[(pkey >> a.page_shift) - page0]);
                 const char *base = (j < NI ? kc_b : vc_b) + (uint64_t)pg * ppage;
@@ -414,13 +350,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
         return bad;
     };
 
-    // Barrier that orders LDS only (the loads in flight are tracked by wait_tile).
-    auto lds_barrier = []() TA_INLINE {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    };
-
     // One pass over every tile of the part. At the top of iteration t the barrier publishes
     // tile t (every wavefront has waited for its own loads of it) and retires tile t - 1, whose
     // stage then takes the loads of tile t + NS - 1.
@@ -472,15 +401,15 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnArgs a) {
     }
 }
 
-hipError_t launch_attn_bf16(const AttnArgs &a, int nw, hipStream_t s) {
+hipError_t launch_attn_tree(const AttnArgs &a, int nw, hipStream_t s) {
     if (a.n_splits == 0 || a.B == 0) return hipSuccess;
     const dim3 grid(a.n_splits, a.Hkv * a.n_rb, a.B);
 #define TA_LAUNCH(DD, NN)                                                                        \
     do {                                                                                         \
         if (a.block_table)                                                                       \
-            hipLaunchKernelGGL((attn_bf16_kernel<DD, NN, true>), grid, dim3(NN * 64), 0, s, a);  \
+            hipLaunchKernelGGL((attn_tree_kernel<DD, NN, true>), grid, dim3(NN * 64), 0, s, a);  \
         else                                                                                     \
-            hipLaunchKernelGGL((attn_bf16_kernel<DD, NN, false>), grid, dim3(NN * 64), 0, s, a); \
+            hipLaunchKernelGGL((attn_tree_kernel<DD, NN, false>), grid, dim3(NN * 64), 0, s, a); \
     } while (0)
     if (a.D == 128) {
         if (nw == 2) TA_LAUNCH(128, 2);

@@ -14,8 +14,10 @@ constexpr int kRowsPerWave = 32;
 constexpr int kPageCache = 2048;
 
 // Device-side view of one attention launch. Part p (0 <= p < n_splits) covers prefix keys
-// [p * chunk, min((p + 1) * chunk, seq_len)) when with_prefix is set, and the last part also
-// covers the masked tree keys when with_tree is set. Partial outputs go to
+// [p * chunk, min((p + 1) * chunk, seq_len)) when with_prefix is set (the bf16 prefix kernel
+// stops at the last multiple of kKeyTile of seq_len), and the last part also covers the masked
+// tree keys when with_tree is set. With tail_only (masked kernel, one part) the prefix keys are
+// [seq_len rounded down to kKeyTile, seq_len) instead. Partial outputs go to
 // out_o[part][row][D] and out_lse[part][row], row = (b * T + node) * Hq + head.
 struct AttnArgs {
     const void *q;
@@ -32,6 +34,7 @@ struct AttnArgs {
     int32_t n_splits;
     int32_t with_prefix;
     int32_t with_tree;
+    int32_t tail_only;
     int32_t chunk;      // prefix keys per split (multiple of kKeyTile)
     int32_t n_rb;       // row blocks per (b, kv-head)
     float scale;        // logit scale
@@ -57,7 +60,8 @@ struct MergeArgs {
 
 hipError_t launch_mask(const int32_t *parent, int B, int T, uint64_t *mask, int32_t *err,
                        hipStream_t s);
-hipError_t launch_attn_bf16(const AttnArgs &a, int nw, hipStream_t s);
+hipError_t launch_attn_prefix(const AttnArgs &a, int nw, hipStream_t s);
+hipError_t launch_attn_tree(const AttnArgs &a, int nw, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &m, bool out_bf16, hipStream_t s);
 
