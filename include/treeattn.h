@@ -115,7 +115,7 @@ int tree_mask_build(const int32_t *parent, int B, int T, uint64_t *mask, int32_t
 
 /*
  * Host-only. Bytes of workspace that tree_attn_prefix and tree_attn_forward need for ``p``
- * (one partial output and log-sum-exp per split, fp32). Writes *bytes; returns TA_EINVAL /
+ * (one partial output and log-sum-exp per part, fp32; num_splits + 1 parts). Writes *bytes; returns TA_EINVAL /
  * TA_EUNSUPPORTED for a problem the other calls would reject.
  */
 int tree_attn_workspace_size(const ta_problem *p, size_t *bytes);
@@ -168,10 +168,12 @@ int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t
  * The divide step of tree_attn_forward on its own: every prefix split and the masked tree part
  * write their partial (O, LSE) into ``ws`` (LongSpec page, "Fast tree attention", splitting the
  * key-value pairs; the prefix is further split along its length). Workspace layout, with
- * P = tree_attn_num_splits() parts and rows = B * T * Hq: fp32 O parts [P][rows][D] at byte 0,
- * then fp32 LSE parts [P][rows] at byte tree_attn_workspace_lse_offset(). Part p covers one
- * chunk of every sequence's prefix; the last part also covers the masked tree keys. A caller
- * that shards the prefix over several devices exchanges these partials.
+ * S = tree_attn_num_splits(), P = S + 1 parts and rows = B * T * Hq: fp32 O parts
+ * [P][rows][D] at byte 0, then fp32 LSE parts [P][rows] at byte
+ * tree_attn_workspace_lse_offset(). Part p < S covers one chunk of every sequence's prefix
+ * (bf16: up to the last multiple of 64 of the sequence's length); part S covers the masked tree
+ * keys and, for bf16, the prefix keys past that multiple of 64. An empty part has O = 0 and
+ * LSE = -inf. A caller that shards the prefix over several devices exchanges these partials.
  */
 int tree_attn_partials(const ta_problem *p, void *ws, size_t ws_bytes, int32_t *err_flag,
                        hipStream_t stream);

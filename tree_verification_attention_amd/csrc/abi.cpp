@@ -201,13 +201,16 @@ int launch_prefix_parts(const ta_problem *p, const Plan &pl, int32_t *err, float
 int launch_last_part(const ta_problem *p, const Plan &pl, int32_t *err, float *o, float *l,
                      bool tail, bool tree, hipStream_t s) {
     AttnArgs a = make_args(p, pl, err);
+    // small work: 64 rows per workgroup (two wavefronts) spreads it over more compute units
+    const int R = p->T * (p->Hq / p->Hkv);
+    a.n_rb = (R + 63) / 64;
     a.n_splits = 1;
     a.with_prefix = tail && p->dtype == TA_BF16;
     a.tail_only = 1;
     a.with_tree = tree;
     a.out_o = o;
     a.out_lse = l;
-    return status(p->dtype == TA_BF16 ? ta::launch_attn_tree(a, pl.nw, s) : ta::launch_attn_f32(a, s));
+    return status(p->dtype == TA_BF16 ? ta::launch_attn_tree(a, 2, s) : ta::launch_attn_f32(a, s));
 }
 
 }  // namespace
