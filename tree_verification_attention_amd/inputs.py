@@ -333,3 +333,74 @@ def tree_depths(parent: np.ndarray) -> np.ndarray:
     for i, p in enumerate(parent):
         d[i] = 1 if p < 0 else d[p] + 1
     return d
+
+
+# ---------------------------------------------------------------------------------------------
+# greedy acceptance and commit operands
+
+@dataclasses.dataclass
+class AcceptCase:
+    """Operands of greedy tree acceptance: target logits [B, T + 1, V] (row 0 = the position of
+    the last committed token, row i + 1 = tree node i; bf16 bits or float32), draft tokens and
+    parent arrays [B, T]."""
+
+    logits: np.ndarray
+    draft: np.ndarray
+    parent: np.ndarray
+    dtype: str
+
+    @property
+    def V(self) -> int:
+        return self.logits.shape[-1]
+
+
+def make_accept_case(B: int, T: int, V: int, seed: int = 0, *, tree: str = "bounded",
+                     dtype: str = "bf16", plant: float = 0.8, ties: float = 0.15,
+                     blocks: float = 0.05, depth_cap: int = 8, branch_cap: int = 4) -> AcceptCase:
+    """Logits N(0, 1) clipped to [-6, 6]; draft tokens uniform in [0, V). In every row, with
+    probability ``plant``, one child of that row's node (row 0: a root-attached node) gets its
+    draft token's logit set to 7 -- the row's unique maximum by construction, so the child agrees
+    with the target; with probability ``ties`` a second random index of that row is also set to
+    7 (equal maxima: the first index wins); with probability ``blocks`` two random indices are set
+    to 7.5 instead (a maximum no draft token is likely to hit). Nothing here computes an argmax."""
+    rng = np.random.Generator(np.random.PCG64([seed, 7]))
+    wl = Workload("accept", B=B, Hq=1, Hkv=1, D=64, T=T, L=0, tree=tree, depth_cap=depth_cap,
+                  branch_cap=branch_cap)
+    parent = np.stack([make_tree(rng, wl) for _ in range(B)]).astype(np.int32)
+    draft = rng.integers(0, V, size=(B, T), dtype=np.int32)
+    x = rng.standard_normal((B, T + 1, V), dtype=np.float32)
+    np.clip(x, -6.0, 6.0, out=x)
+    for b in range(B):
+        kids = [[] for _ in range(T + 1)]
+        for i in range(T):
+            kids[int(parent[b, i]) + 1].append(i)
+        for r in range(T + 1):
+            if kids[r] and rng.random() < plant:
+                c = kids[r][int(rng.integers(len(kids[r])))]
+                x[b, r, draft[b, c]] = 7.0
+                if rng.random() < ties:
+                    x[b, r, int(rng.integers(V))] = 7.0
+            if rng.random() < blocks:
+                x[b, r, rng.integers(V, size=2)] = 7.5
+    logits = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    return AcceptCase(logits=logits, draft=draft, parent=parent, dtype=dtype)
+
+
+def random_paths(parent: np.ndarray, rng: np.random.Generator, max_len=None):
+    """One root path per sequence (root first) ending at a random node, or empty: the shape of
+    what greedy acceptance commits. Returns (path [B, T] padded with -1, accept_len [B])."""
+    B, T = parent.shape
+    path = np.full((B, T), -1, np.int32)
+    n = np.zeros(B, np.int32)
+    for b in range(B):
+        end = int(rng.integers(-1, T))
+        chain = []
+        while end >= 0:
+            chain.append(end)
+            end = int(parent[b, end])
+        chain.reverse()
+        if max_len is not None:
+            chain = chain[:max_len]
+        path[b, :len(chain)] = chain
+        n[b] = len(chain)
+    return path, n
