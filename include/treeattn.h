@@ -57,6 +57,7 @@ typedef enum ta_dtype {
 #define TA_DEV_BAD_PARENT 1u   /* parent[b][i] outside [-1, i-1] */
 #define TA_DEV_BAD_LEN 2u      /* seq_lens[b] outside [0, capacity] */
 #define TA_DEV_BAD_PAGE 4u     /* a block-table entry used by a prefix outside [0, num_pages) */
+#define TA_DEV_BAD_COMMIT 8u   /* a commit past the cache capacity, or a path entry outside [0, T) */
 
 /* Largest tree the kernels accept. */
 #define TA_MAX_TREE 256
@@ -188,6 +189,48 @@ int tree_attn_combine(const ta_problem *p, const void *ws, size_t ws_bytes, void
 
 /* Host-only. Byte offset of the LSE parts inside the workspace of ``p``. */
 int tree_attn_workspace_lse_offset(const ta_problem *p, size_t *offset);
+
+/*
+ * Greedy tree acceptance (textbook page, "Faster decoding", greedy verification contract: accept
+ * the longest draft prefix that agrees with the target's greedy tokens, then emit the target's
+ * greedy token at the first disagreement), on a draft tree.
+ *   logits      [B, T + 1, V] of ``dtype`` (TA_BF16 or TA_F32): row (b, 0) holds the target's
+ *               logits at sequence b's last committed token, row (b, i + 1) at tree node i.
+ *               ``row_stride`` (elements, >= V) separates consecutive rows; the base and every
+ *               row must be 16-byte aligned.
+ *   draft       int32 [B, T]: the draft token of every node.
+ *   parent      int32 [B, T]: topological parent array (-1 = attached to the committed prefix).
+ * Outputs (device memory, caller-owned):
+ *   greedy      int32 [B, T + 1]: argmax of every row -- the first index holding the maximum of
+ *               the row's non-NaN entries (a row of NaN only gives 0).
+ *   accept_len  int32 [B]: nodes on the committed path.
+ *   path        int32 [B, T]: the committed path, root first; -1 past accept_len. Node i is
+ *               accepted iff draft[i] equals the greedy token of its parent's row (row 0 for a
+ *               root-attached node) and its parent is accepted; the path ends at the deepest
+ *               accepted node (the smallest index among equally deep ones).
+ *   next_token  int32 [B]: the greedy token of the last path node's row (row 0 if none).
+ * Parents outside [-1, i-1] set TA_DEV_BAD_PARENT and count as -1. 1 <= T <= TA_MAX_TREE.
+ */
+int tree_greedy_accept(const void *logits, int dtype, int64_t row_stride, int B, int T, int V,
+                       const int32_t *draft, const int32_t *parent, int32_t *greedy,
+                       int32_t *accept_len, int32_t *path, int32_t *next_token,
+                       int32_t *err_flag, hipStream_t stream);
+
+/*
+ * Accepted-path KV commit (textbook page, "Faster decoding", reserve / execute / commit: only
+ * the accepted draft prefix's target KV is committed, rejected branches are released). For every
+ * sequence b, the tree K/V rows path[b][j], j < accept_len[b], are copied to cache positions
+ * seq_lens[b] + j of k_cache / v_cache, and new_seq_lens[b] = seq_lens[b] + accept_len[b].
+ * Shapes, dtype, strides, seq_lens, the cache layout (contiguous, or page pool + block_table whose
+ * entries for the new positions the caller has reserved) and the tree K/V come from ``p``;
+ * k_cache / v_cache are the writable buffers that p->k_cache / p->v_cache describe. A sequence
+ * whose commit would pass the capacity (or with accept_len outside [0, T]) writes nothing, keeps
+ * its length and sets TA_DEV_BAD_COMMIT; a path entry outside [0, T) sets it and is skipped.
+ * new_seq_lens may alias p->seq_lens (it is written after every copy has read the old lengths).
+ */
+int tree_kv_commit(const ta_problem *p, void *k_cache, void *v_cache, const int32_t *path,
+                   const int32_t *accept_len, int32_t *new_seq_lens, int32_t *err_flag,
+                   hipStream_t stream);
 
 /* Static description of a status code. Never NULL. */
 const char *tree_attn_status_string(int status);

@@ -18,14 +18,15 @@ LIB_PATH = os.path.join(_PKG, "libtreeattn.so")
 
 TA_OK, TA_EINVAL, TA_EUNSUPPORTED, TA_EWORKSPACE, TA_EHIP = range(5)
 TA_BF16, TA_F32 = 0, 1
-TA_DEV_BAD_PARENT, TA_DEV_BAD_LEN, TA_DEV_BAD_PAGE = 1, 2, 4
+TA_DEV_BAD_PARENT, TA_DEV_BAD_LEN, TA_DEV_BAD_PAGE, TA_DEV_BAD_COMMIT = 1, 2, 4, 8
 TA_MAX_TREE = 256
 
 # Functions the header declares (checked against the shared object by the test suite).
 EXPORTS = ("tree_mask_build", "tree_attn_workspace_size", "tree_attn_num_splits",
            "tree_attn_prefix", "tree_attn_tree", "tree_attn_merge", "tree_attn_forward",
            "tree_attn_partials", "tree_attn_combine", "tree_attn_workspace_lse_offset",
-           "tree_attn_status_string", "tree_attn_abi_version")
+           "tree_attn_status_string", "tree_attn_abi_version", "tree_greedy_accept",
+           "tree_kv_commit")
 
 
 class TreeAttnError(RuntimeError):
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH):
     lib.tree_attn_status_string.argtypes = [I]
     lib.tree_attn_status_string.restype = ctypes.c_char_p
     lib.tree_attn_abi_version.argtypes = []
+    lib.tree_greedy_accept.argtypes = [P, I, ctypes.c_int64, I, I, I, P, P, P, P, P, P, P, P]
+    lib.tree_kv_commit.argtypes = [PP, P, P, P, P, P, P, P]
     for fn in EXPORTS:
         if fn not in ("tree_attn_status_string",):
             getattr(lib, fn).restype = ctypes.c_int
@@ -270,3 +273,41 @@ def mask_build(parent, err=None):
         _gpu(parent, "parent", torch.int32), B, T, mask.data_ptr(), _gpu(err, "err", torch.int32),
         _stream()))
     return mask
+
+
+def greedy_accept(logits, draft, parent, *, err=None):
+    """Greedy tree acceptance. logits [B, T + 1, V] (bf16 or fp32; row 0 = the last committed
+    token, row i + 1 = tree node i), draft / parent int32 [B, T]
+    -> (greedy [B, T + 1], accept_len [B], path [B, T], next_token [B]), all int32."""
+    if logits.dtype not in _DT:
+        raise TypeError(f"unsupported logits dtype {logits.dtype}")
+    if logits.stride(-1) != 1 or logits.stride(0) != logits.shape[1] * logits.stride(1):
+        raise ValueError("logits rows must be evenly strided with a contiguous last dimension")
+    B, T1, V = logits.shape
+    T = T1 - 1
+    dev = logits.device
+    greedy = torch.empty((B, T + 1), dtype=torch.int32, device=dev)
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty((B, T), dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    _check("tree_greedy_accept", load().tree_greedy_accept(
+        _gpu(logits, "logits"), _DT[logits.dtype], logits.stride(1), B, T, V,
+        _gpu(draft, "draft", torch.int32), _gpu(parent, "parent", torch.int32), greedy.data_ptr(),
+        n.data_ptr(), path.data_ptr(), nxt.data_ptr(), _gpu(err, "err", torch.int32), _stream()))
+    return greedy, n, path, nxt
+
+
+def kv_commit(k_cache, v_cache, seq_lens, k_tree, v_tree, path, accept_len, *, block_table=None,
+              page_size=None, new_seq_lens=None, err=None):
+    """Accepted-path KV commit: writes the path's tree K/V rows into k_cache / v_cache (in place)
+    at positions seq_lens[b] + j and returns the new lengths (``new_seq_lens`` may be
+    ``seq_lens`` itself)."""
+    # the commit reads neither queries nor parents: k_tree and path stand in for their shapes
+    p = make_problem(k_tree, k_cache, v_cache, seq_lens, k_tree, v_tree, path,
+                     block_table=block_table, page_size=page_size)
+    out = new_seq_lens if new_seq_lens is not None else torch.empty_like(seq_lens)
+    _check("tree_kv_commit", load().tree_kv_commit(
+        ctypes.byref(p), _gpu(k_cache, "k_cache"), _gpu(v_cache, "v_cache"),
+        _gpu(path, "path", torch.int32), _gpu(accept_len, "accept_len", torch.int32),
+        _gpu(out, "new_seq_lens", torch.int32), _gpu(err, "err", torch.int32), _stream()))
+    return out

@@ -352,4 +352,57 @@ int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t
     return tree_attn_combine(p, ws, ws_bytes, o, lse, stream);
 }
 
+int tree_greedy_accept(const void *logits, int dtype, int64_t row_stride, int B, int T, int V,
+                       const int32_t *draft, const int32_t *parent, int32_t *greedy,
+                       int32_t *accept_len, int32_t *path, int32_t *next_token,
+                       int32_t *err_flag, hipStream_t stream) {
+    if (dtype != TA_BF16 && dtype != TA_F32) return TA_EUNSUPPORTED;
+    if (B < 0 || T < 1 || T > TA_MAX_TREE || V < 1 || row_stride < V) return TA_EINVAL;
+    if (B == 0) return TA_OK;
+    if (!logits || !draft || !parent || !greedy || !accept_len || !path || !next_token)
+        return TA_EINVAL;
+    const int es = elem_size(dtype);
+    if (!aligned16(logits) || (row_stride * es) % 16) return TA_EINVAL;
+    return status(ta::launch_greedy_accept(logits, dtype == TA_BF16, row_stride, B, T, V, draft,
+                                           parent, greedy, accept_len, path, next_token, err_flag,
+                                           stream));
+}
+
+int tree_kv_commit(const ta_problem *p, void *k_cache, void *v_cache, const int32_t *path,
+                   const int32_t *accept_len, int32_t *new_seq_lens, int32_t *err_flag,
+                   hipStream_t stream) {
+    int rc = check_shape(p);
+    if (rc) return rc;
+    if (p->B == 0) return TA_OK;
+    if ((rc = check_prefix(p)) || (rc = check_tree(p))) return rc;
+    if (!k_cache || !v_cache || !path || !accept_len || !new_seq_lens) return TA_EINVAL;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return TA_EINVAL;
+    const Plan pl = make_plan(p);
+    ta::CommitArgs c{};
+    c.kt = p->k_tree;
+    c.vt = p->v_tree;
+    c.kt_sb = p->kt_sb;
+    c.kt_st = p->kt_st;
+    c.kt_sh = p->kt_sh;
+    c.kc = k_cache;
+    c.vc = v_cache;
+    c.kv_s0 = p->kv_s0;
+    c.kv_s1 = p->kv_s1;
+    c.kv_s2 = p->kv_s2;
+    c.block_table = p->block_table;
+    c.max_blocks = p->max_blocks;
+    c.page_shift = p->block_table ? ilog2(p->page_size) : 0;
+    c.page_mask = p->block_table ? p->page_size - 1 : 0;
+    c.num_pages = p->num_pages;
+    c.capacity = pl.capacity;
+    c.seq_lens = p->seq_lens;
+    c.accept_len = accept_len;
+    c.path = path;
+    c.T = p->T;
+    c.es = elem_size(p->dtype);
+    c.row_bytes = p->D * c.es;
+    c.err = err_flag;
+    return status(ta::launch_commit(c, p->B, p->Hkv, new_seq_lens, stream));
+}
+
 }  // extern "C"

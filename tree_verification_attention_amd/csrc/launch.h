@@ -58,11 +58,30 @@ struct MergeArgs {
     float *lse;
 };
 
+// Accepted-path KV commit: tree K/V rows path[b][j] (j < accept_len[b]) go to cache position
+// seq_lens[b] + j of sequence b (contiguous cache or page pool), row_bytes = D * es per head.
+struct CommitArgs {
+    const void *kt, *vt;
+    int64_t kt_sb, kt_st, kt_sh;
+    void *kc, *vc;
+    int64_t kv_s0, kv_s1, kv_s2;
+    const int32_t *block_table;
+    int32_t max_blocks, page_shift, page_mask, num_pages, capacity;
+    const int32_t *seq_lens, *accept_len, *path;
+    int32_t T, es, row_bytes;
+    int32_t *err;
+};
+
 hipError_t launch_mask(const int32_t *parent, int B, int T, uint64_t *mask, int32_t *err,
                        hipStream_t s);
 hipError_t launch_attn_prefix(const AttnArgs &a, int nw, hipStream_t s);
 hipError_t launch_attn_tree(const AttnArgs &a, int nw, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &m, bool out_bf16, hipStream_t s);
+hipError_t launch_greedy_accept(const void *logits, bool bf16, int64_t row_stride, int B, int T,
+                                int V, const int32_t *draft, const int32_t *parent, int32_t *greedy,
+                                int32_t *accept_len, int32_t *path, int32_t *next_token,
+                                int32_t *err, hipStream_t s);
+hipError_t launch_commit(const CommitArgs &c, int B, int Hkv, int32_t *new_lens, hipStream_t s);
 
 }  // namespace ta
