@@ -140,16 +140,16 @@ def time_case(case, steps, warmup, label):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-    # the dominant kernel alone, same stream, same events; before each launch a 512 MiB fill
+    # the dominant kernel alone, same stream, same events; before each launch a 512 MiB read
     # (outside the events) evicts the 256 MB last-level cache and the L2s
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    evict = make_evict()
     for _ in range(warmup):
         part()
     torch.cuda.synchronize()
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for i in range(steps):
-        flush.zero_()
+        evict()
         kev[i][0].record(stream)
         part()
         kev[i][1].record(stream)
@@ -162,6 +162,86 @@ def time_case(case, steps, warmup, label):
           flush=True)
     return {"wall_s": wall, "step_us": step_us, "kernel_us": kern_us,
             "n_splits": _lib.num_splits(p), "ws_bytes": ws_bytes}
+
+
+def make_evict():
+    """A function that reads FLUSH_BYTES of device memory. A read, not a fill: it leaves the caches
+    holding clean lines of another buffer, so the timed kernel pays for no write-back of them."""
+    import torch
+
+    buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    return lambda: torch.sum(buf, dim=0, out=out)
+
+
+def time_next_rows(steps, warmup, seed):
+    """Greedy tree acceptance over a Llama-3-size vocabulary and the accepted-path KV commit, at
+    the headline batch / tree / head shape; each call timed with HIP events after a cache-evicting read."""
+    import numpy as np
+    import torch
+
+    import oracle.accept as oacc
+    from tree_verification_attention_amd import _lib, inputs
+
+    B, T, V = 4, 64, 128256
+    ac = inputs.make_accept_case(B, T, V, seed)
+    lg = torch.from_numpy(ac.logits.view(np.int16)).view(torch.bfloat16).cuda()
+    draft, parent = torch.from_numpy(ac.draft).cuda(), torch.from_numpy(ac.parent).cuda()
+    evict = make_evict()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(steps):
+            evict()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return statistics.mean(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+    print("[bench] greedy acceptance", file=sys.stderr, flush=True)
+    acc_ws = torch.empty(_lib.greedy_accept_workspace_size(lg.dtype, B, T, V), dtype=torch.uint8,
+                         device="cuda")
+    acc_us = timed(lambda: _lib.greedy_accept(lg, draft, parent, ws=acc_ws))
+    _, n_gpu, path_gpu, _ = _lib.greedy_accept(lg, draft, parent)
+    acc_bytes = B * (T + 1) * V * 2 + 8 * B * T + 4 * B * (T + 1) + 12 * B + 4 * B * T
+    t0 = time.perf_counter()
+    oacc.greedy_accept(ac.logits, ac.draft, ac.parent, "bf16")
+    cpu_s = time.perf_counter() - t0
+    del lg
+    torch.cuda.empty_cache()
+
+    wl = inputs.Workload("commit", B=B, Hq=32, Hkv=8, D=128, T=T, L=4096)
+    cc = inputs.make_case(wl, seed, pad="finite", lcap=4096 + T)
+    dv = lambda a: (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+                    if a.dtype == np.uint16 else torch.from_numpy(a).cuda())
+    kc, vc, kt, vt = dv(cc.k_cache), dv(cc.v_cache), dv(cc.k_tree), dv(cc.v_tree)
+    lens = dv(cc.seq_lens)
+    path, n = inputs.random_paths(cc.parent, np.random.default_rng(seed))
+    path_d, n_d = dv(path), dv(n)
+    out = torch.empty_like(lens)
+    print("[bench] kv commit", file=sys.stderr, flush=True)
+    com_us = timed(lambda: _lib.kv_commit(kc, vc, lens, kt, vt, path_d, n_d, new_seq_lens=out))
+    com_bytes = int(n.sum()) * 8 * 128 * 2 * 2 * 2 + 12 * B + 4 * B * T
+    return {
+        "greedy_accept": {
+            "workload": f"B={B}, T={T} bounded tree, vocab {V}, bf16 logits",
+            "us": round(acc_us, 2), "algorithmic_bytes": acc_bytes,
+            "achieved_gbs": round(acc_bytes / (acc_us * 1e-6) / 1e9, 1), "peak_gbs": HBM_PEAK_GBS,
+            "frac": round(acc_bytes / (acc_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "mean_accept_len": float(n_gpu.float().mean().item()),
+            "cpu_oracle_s": round(cpu_s, 3)},
+        "kv_commit": {
+            "workload": f"B={B}, Hkv=8, D=128 bf16, contiguous cache, {int(n.sum())} rows committed",
+            "us": round(com_us, 2), "algorithmic_bytes": com_bytes,
+            "note": "latency-bound: a few hundred KB move per call"},
+    }
 
 
 def pct(xs, q):
@@ -275,7 +355,7 @@ def parse_pmc(fetch_dir, write_dir, workload):
     os.makedirs(PROFILES, exist_ok=True)
     out = traffic_path(workload)
     run = (f"python3 bench.py --workload {workload} --steps 4 --warmup 1 --no-secondary "
-           f"--no-cpu-baseline --copy-calibration")
+           f"--no-cpu-baseline --no-next-rows --copy-calibration")
     with open(out, "w") as f:
         f.write(f"# HBM traffic of one tree_attn_partials call ({KERNEL_NAME} + {TREE_KERNEL_NAME} "
                 f"dispatch) on workload {workload}.\n"
@@ -321,7 +401,7 @@ def stats_summary(stats_dir, workload, steps):
         f"# rocprofv3 kernel statistics, workload {workload}",
         f"# command: rocprofv3 --kernel-trace --stats -d STATS_DIR -o run --output-format csv -- "
         f"python3 bench.py --workload {workload} --steps {steps} --warmup 5 --no-secondary "
-        f"--no-cpu-baseline",
+        f"--no-cpu-baseline --no-next-rows",
         f"# summary: python3 bench.py --workload {workload} --steps {steps} --stats-summary STATS_DIR",
         "",
         "kernel | calls | average us | min us | max us",
@@ -333,7 +413,7 @@ def stats_summary(stats_dir, workload, steps):
         "",
         f"{KERNEL_NAME}, timed fused-forward loop ({len(fused)} launches, no cache flush): "
         f"average {statistics.mean(fused):.2f} us",
-        f"{KERNEL_NAME}, kernel-alone loop ({len(alone)} launches, 512 MiB flush before each): "
+        f"{KERNEL_NAME}, kernel-alone loop ({len(alone)} launches, 512 MiB evicting read before each): "
         f"average {statistics.mean(alone):.2f} us, median {statistics.median(alone):.2f} us",
         f"{TREE_KERNEL_NAME}, same loop: average {statistics.mean(talone):.2f} us",
         f"sum per tree_attn_partials call: {statistics.mean(alone) + statistics.mean(talone):.2f} us",
@@ -354,6 +434,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the drawn-length (32k..64k) variant of the workload")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip timing greedy acceptance and the KV commit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB copies (reference for HBM counters)")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -444,6 +526,9 @@ def main():
                              "tb_per_s": round(w2["step_bytes"] / (ms2 * 1e-3) / 1e12, 4),
                              "kernel_avg_us": round(statistics.mean(r2["kernel_us"]), 2)}
         del case2
+        torch.cuda.empty_cache()
+    if not args.no_next_rows and wl.name == "gqa_64k_pinned":
+        line["next_rows"] = time_next_rows(args.steps, args.warmup, args.seed)
         torch.cuda.empty_cache()
     if args.copy_calibration:
         copy_calibration()

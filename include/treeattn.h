@@ -209,12 +209,18 @@ int tree_attn_workspace_lse_offset(const ta_problem *p, size_t *offset);
  *               root-attached node) and its parent is accepted; the path ends at the deepest
  *               accepted node (the smallest index among equally deep ones).
  *   next_token  int32 [B]: the greedy token of the last path node's row (row 0 if none).
- * Parents outside [-1, i-1] set TA_DEV_BAD_PARENT and count as -1. 1 <= T <= TA_MAX_TREE.
+ * ``ws``: device memory of at least tree_greedy_accept_workspace_size() bytes, 256-byte aligned
+ * (each row is scanned in several chunks whose winners meet there); otherwise TA_EWORKSPACE.
+ * Parents outside [-1, i-1] set TA_DEV_BAD_PARENT and count as -1. 1 <= T <= TA_MAX_TREE,
+ * 0 <= B <= 65535.
  */
 int tree_greedy_accept(const void *logits, int dtype, int64_t row_stride, int B, int T, int V,
-                       const int32_t *draft, const int32_t *parent, int32_t *greedy,
-                       int32_t *accept_len, int32_t *path, int32_t *next_token,
+                       const int32_t *draft, const int32_t *parent, void *ws, size_t ws_bytes,
+                       int32_t *greedy, int32_t *accept_len, int32_t *path, int32_t *next_token,
                        int32_t *err_flag, hipStream_t stream);
+
+/* Host-only. Workspace bytes tree_greedy_accept needs for these sizes on the current device. */
+int tree_greedy_accept_workspace_size(int dtype, int B, int T, int V, size_t *bytes);
 
 /*
  * Accepted-path KV commit (textbook page, "Faster decoding", reserve / execute / commit: only

@@ -85,6 +85,59 @@ def test_greedy_accept_ragged_vocab_strided_rows_nan_and_inf():
     check_accept(case, "ragged vocab", pad_to=1008)
 
 
+def test_greedy_accept_ties_and_nan_spread_over_the_row_chunks():
+    # rows of a large vocabulary are scanned in several chunks: equal maxima placed all over the
+    # row (the first must win, whichever chunk holds it), rows whose first half is NaN, and
+    # maxima at the very first and very last entries
+    case = inputs.make_accept_case(4, 64, 128256, 9, plant=0.8)
+    x = inputs.bf16_bits_to_f32(case.logits)
+    rng = np.random.default_rng(4)
+    V = x.shape[-1]
+    for b in range(4):
+        for r in range(0, 65, 3):
+            idx = rng.choice(V, size=int(rng.integers(2, 9)), replace=False)
+            x[b, r, idx] = 11.0
+    x[0, 1, :V // 2] = np.nan
+    x[1, 2, :] = -3.0
+    x[1, 2, V - 1] = 12.0
+    x[2, 4, 0] = 12.0
+    x[3, 7, :] = np.nan
+    x[3, 8, 1:] = np.nan
+    x[0, 9, :] = -np.abs(x[0, 9, :]) - 0.5      # every entry negative
+    x[0, 10, :] = -1.0                           # maximum 0 held by -0 before +0: they tie
+    x[0, 10, 70001] = -0.0
+    x[0, 10, 90001] = 0.0
+    x[0, 11, 5] = np.nan                         # a NaN and a larger value later in the row
+    x[0, 11, 100000] = 20.0
+    case.logits = inputs.f32_to_bf16_bits(x)
+    check_accept(case, "ties over chunks")
+
+
+def test_greedy_accept_f32_special_rows():
+    case = inputs.make_accept_case(2, 12, 40000, 3, dtype="f32", plant=0.9)
+    x = case.logits
+    x[0, 1, :] = -2.0
+    x[0, 1, 30000] = -0.0
+    x[0, 1, 35000] = 0.0
+    x[0, 2, :] = np.nan
+    x[0, 3, :] = -np.inf
+    x[0, 3, 39999] = np.nan
+    x[1, 4, 100] = np.inf
+    x[1, 4, 39000] = np.inf
+    x[1, 5, 7] = np.nan
+    x[1, 5, 20000] = 50.0
+    check_accept(case, "f32 special rows")
+
+
+def test_greedy_accept_rejects_a_short_workspace():
+    case = inputs.make_accept_case(4, 64, 128256, 2)
+    lg = dev(case.logits)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(_lib.TreeAttnError) as ei:
+        _lib.greedy_accept(lg, dev(case.draft), dev(case.parent), ws=ws)
+    assert ei.value.status == _lib.TA_EWORKSPACE
+
+
 def test_greedy_accept_bad_parent_sets_flag():
     case = inputs.make_accept_case(2, 8, 128, 1)
     case.parent[1, 4] = 6

@@ -26,6 +26,7 @@ EXPORTS = ("tree_mask_build", "tree_attn_workspace_size", "tree_attn_num_splits"
            "tree_attn_prefix", "tree_attn_tree", "tree_attn_merge", "tree_attn_forward",
            "tree_attn_partials", "tree_attn_combine", "tree_attn_workspace_lse_offset",
            "tree_attn_status_string", "tree_attn_abi_version", "tree_greedy_accept",
+           "tree_greedy_accept_workspace_size",
            "tree_kv_commit")
 
 
@@ -82,7 +83,8 @@ def load(path: str = LIB_PATH):
     lib.tree_attn_status_string.argtypes = [I]
     lib.tree_attn_status_string.restype = ctypes.c_char_p
     lib.tree_attn_abi_version.argtypes = []
-    lib.tree_greedy_accept.argtypes = [P, I, ctypes.c_int64, I, I, I, P, P, P, P, P, P, P, P]
+    lib.tree_greedy_accept.argtypes = [P, I, ctypes.c_int64, I, I, I, P, P, P, S, P, P, P, P, P, P]
+    lib.tree_greedy_accept_workspace_size.argtypes = [I, I, I, I, ctypes.POINTER(S)]
     lib.tree_kv_commit.argtypes = [PP, P, P, P, P, P, P, P]
     for fn in EXPORTS:
         if fn not in ("tree_attn_status_string",):
@@ -275,9 +277,20 @@ def mask_build(parent, err=None):
     return mask
 
 
-def greedy_accept(logits, draft, parent, *, err=None):
+def greedy_accept_workspace_size(dtype, B: int, T: int, V: int) -> int:
+    """Workspace bytes (at least 256) that greedy_accept needs for these sizes."""
+    if dtype not in _DT:
+        raise TypeError(f"unsupported logits dtype {dtype}")
+    need = ctypes.c_size_t(0)
+    _check("tree_greedy_accept_workspace_size", load().tree_greedy_accept_workspace_size(
+        _DT[dtype], B, T, V, ctypes.byref(need)))
+    return max(need.value, 256)
+
+
+def greedy_accept(logits, draft, parent, *, ws=None, err=None):
     """Greedy tree acceptance. logits [B, T + 1, V] (bf16 or fp32; row 0 = the last committed
-    token, row i + 1 = tree node i), draft / parent int32 [B, T]
+    token, row i + 1 = tree node i), draft / parent int32 [B, T]; ``ws`` (optional) is a device
+    buffer of greedy_accept_workspace_size() bytes, allocated per call when omitted
     -> (greedy [B, T + 1], accept_len [B], path [B, T], next_token [B]), all int32."""
     if logits.dtype not in _DT:
         raise TypeError(f"unsupported logits dtype {logits.dtype}")
@@ -290,10 +303,14 @@ def greedy_accept(logits, draft, parent, *, err=None):
     n = torch.empty(B, dtype=torch.int32, device=dev)
     path = torch.empty((B, T), dtype=torch.int32, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(greedy_accept_workspace_size(logits.dtype, B, T, V), dtype=torch.uint8,
+                         device=dev)
     _check("tree_greedy_accept", load().tree_greedy_accept(
         _gpu(logits, "logits"), _DT[logits.dtype], logits.stride(1), B, T, V,
-        _gpu(draft, "draft", torch.int32), _gpu(parent, "parent", torch.int32), greedy.data_ptr(),
-        n.data_ptr(), path.data_ptr(), nxt.data_ptr(), _gpu(err, "err", torch.int32), _stream()))
+        _gpu(draft, "draft", torch.int32), _gpu(parent, "parent", torch.int32), _gpu(ws, "ws"),
+        ws.numel() * ws.element_size(), greedy.data_ptr(), n.data_ptr(), path.data_ptr(),
+        nxt.data_ptr(), _gpu(err, "err", torch.int32), _stream()))
     return greedy, n, path, nxt
 
 

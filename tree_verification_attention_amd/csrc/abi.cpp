@@ -352,20 +352,42 @@ int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t
     return tree_attn_combine(p, ws, ws_bytes, o, lse, stream);
 }
 
-int tree_greedy_accept(const void *logits, int dtype, int64_t row_stride, int B, int T, int V,
-                       const int32_t *draft, const int32_t *parent, int32_t *greedy,
-                       int32_t *accept_len, int32_t *path, int32_t *next_token,
-                       int32_t *err_flag, hipStream_t stream) {
+static int check_accept(int dtype, int B, int T, int V) {
     if (dtype != TA_BF16 && dtype != TA_F32) return TA_EUNSUPPORTED;
-    if (B < 0 || T < 1 || T > TA_MAX_TREE || V < 1 || row_stride < V) return TA_EINVAL;
+    if (B < 0 || B > 65535 || T < 1 || T > TA_MAX_TREE || V < 1) return TA_EINVAL;
+    // one workgroup per (row, chunk): the grid must fit its 32-bit dimension
+    if ((int64_t)B * (T + 1) * ta::greedy_accept_chunks(V, dtype == TA_BF16) > INT32_MAX)
+        return TA_EINVAL;
+    return TA_OK;
+}
+
+int tree_greedy_accept_workspace_size(int dtype, int B, int T, int V, size_t *bytes) {
+    int rc = check_accept(dtype, B, T, V);
+    if (rc) return rc;
+    if (!bytes) return TA_EINVAL;
+    const int S = ta::greedy_accept_chunks(V, dtype == TA_BF16);
+    *bytes = align256((size_t)B * (T + 1) * S * 8);
+    return TA_OK;
+}
+
+int tree_greedy_accept(const void *logits, int dtype, int64_t row_stride, int B, int T, int V,
+                       const int32_t *draft, const int32_t *parent, void *ws, size_t ws_bytes,
+                       int32_t *greedy, int32_t *accept_len, int32_t *path, int32_t *next_token,
+                       int32_t *err_flag, hipStream_t stream) {
+    int rc = check_accept(dtype, B, T, V);
+    if (rc) return rc;
+    if (row_stride < V) return TA_EINVAL;
     if (B == 0) return TA_OK;
     if (!logits || !draft || !parent || !greedy || !accept_len || !path || !next_token)
         return TA_EINVAL;
     const int es = elem_size(dtype);
     if (!aligned16(logits) || (row_stride * es) % 16) return TA_EINVAL;
-    return status(ta::launch_greedy_accept(logits, dtype == TA_BF16, row_stride, B, T, V, draft,
-                                           parent, greedy, accept_len, path, next_token, err_flag,
-                                           stream));
+    const int S = ta::greedy_accept_chunks(V, dtype == TA_BF16);
+    if (!ws || ((uintptr_t)ws & 255) || ws_bytes < (size_t)B * (T + 1) * S * 8)
+        return TA_EWORKSPACE;
+    return status(ta::launch_greedy_accept(logits, dtype == TA_BF16, row_stride, B, T, V, S, draft,
+                                           parent, static_cast<int2 *>(ws), greedy, accept_len,
+                                           path, next_token, err_flag, stream));
 }
 
 int tree_kv_commit(const ta_problem *p, void *k_cache, void *v_cache, const int32_t *path,

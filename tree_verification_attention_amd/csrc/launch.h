@@ -78,10 +78,12 @@ hipError_t launch_attn_prefix(const AttnArgs &a, int nw, hipStream_t s);
 hipError_t launch_attn_tree(const AttnArgs &a, int nw, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &m, bool out_bf16, hipStream_t s);
+// Chunks per logits row for the argmax (the workspace holds B * (T + 1) * chunks int2 winners).
+int greedy_accept_chunks(int V, bool bf16);
 hipError_t launch_greedy_accept(const void *logits, bool bf16, int64_t row_stride, int B, int T,
-                                int V, const int32_t *draft, const int32_t *parent, int32_t *greedy,
-                                int32_t *accept_len, int32_t *path, int32_t *next_token,
-                                int32_t *err, hipStream_t s);
+                                int V, int S, const int32_t *draft, const int32_t *parent,
+                                int2 *part, int32_t *greedy, int32_t *accept_len, int32_t *path,
+                                int32_t *next_token, int32_t *err, hipStream_t s);
 hipError_t launch_commit(const CommitArgs &c, int B, int Hkv, int32_t *new_lens, hipStream_t s);
 
 }  // namespace ta
