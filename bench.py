@@ -368,6 +368,53 @@ def parse_pmc(fetch_dir, write_dir, workload):
     print(json.dumps(entry, indent=1))
 
 
+ACCEPT_BYTES = 4 * 65 * 128256 * 2   # the bf16 logits rows one greedy-acceptance call reads
+
+
+def accept_stats_summary(stats_dir, steps):
+    """Text summary of a rocprofv3 --kernel-trace --stats run of --next-rows-only."""
+    import re
+
+    paths = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel stats under {stats_dir}")
+    with open(paths[0]) as f:
+        stats = list(csv.DictReader(f))
+    names = ("argmax_kernel", "accept_kernel", "commit_kernel", "lens_kernel")
+    rows = [r for r in stats if any(n in r["Name"] for n in names)]
+    bench = None
+    logs = glob.glob(stats_dir.rstrip("/") + ".log")
+    if logs:
+        m = re.search(r'^\{.*\}$', open(logs[0]).read(), re.M)
+        bench = json.loads(m.group(0)) if m else None
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, "argmax_kernel_greedy_accept_b4_t64_v128256_stats.txt")
+    lines = [
+        "# rocprofv3 kernel statistics, greedy tree acceptance (B=4, T=64, vocab 128256, bf16 "
+        "logits) and accepted-path KV commit (B=4, Hkv=8, D=128 bf16)",
+        f"# command: rocprofv3 --kernel-trace --stats -d STATS_DIR -o run --output-format csv -- "
+        f"python3 bench.py --next-rows-only --steps {steps} --warmup 5",
+        f"# summary: python3 bench.py --steps {steps} --accept-stats-summary STATS_DIR",
+        "",
+        "kernel | calls | average us | min us | max us",
+    ]
+    for r in rows:
+        lines.append(f"{r['Name'][:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f}")
+    arg = [r for r in rows if "argmax_kernel" in r["Name"]]
+    if arg:
+        us = float(arg[0]["AverageNs"]) / 1e3
+        lines += ["", f"argmax_kernel: {ACCEPT_BYTES} logits bytes per call / {us:.2f} us = "
+                      f"{ACCEPT_BYTES / us / 1e3:.1f} GB/s ({ACCEPT_BYTES / us / 1e3 / HBM_PEAK_GBS:.3f} "
+                      f"of {HBM_PEAK_GBS:.0f} GB/s); every call follows a 512 MiB evicting read"]
+    if bench:
+        lines.append(f"bench.py next-row timings (HIP events around each call): "
+                     f"{json.dumps(bench)}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def stats_summary(stats_dir, workload, steps):
     """Text summary of a rocprofv3 --kernel-trace --stats run of this script."""
     import re
@@ -439,6 +486,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB copies (reference for HBM counters)")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--next-rows-only", action="store_true",
+                    help="time only greedy acceptance and the KV commit; print their JSON")
+    ap.add_argument("--accept-stats-summary", metavar="STATS_DIR",
+                    help="summarise a rocprofv3 --stats run of --next-rows-only into profiles/")
     ap.add_argument("--stats-summary", metavar="STATS_DIR",
                     help="write the text summary of a rocprofv3 --kernel-trace --stats run")
     args = ap.parse_args()
@@ -447,6 +498,9 @@ def main():
         stats_summary(args.stats_summary, args.workload, args.steps)
         return
 
+    if args.accept_stats_summary:
+        accept_stats_summary(args.accept_stats_summary, args.steps)
+        return
     if args.parse_pmc:
         parse_pmc(args.parse_pmc[0], args.parse_pmc[1], args.workload)
         return
@@ -466,6 +520,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.next_rows_only:
+        print(json.dumps(time_next_rows(args.steps, args.warmup, args.seed)), flush=True)
+        return
     wl = inputs.WORKLOADS[args.workload]
     print(f"[bench] generating {wl.name} (seed {args.seed})", file=sys.stderr, flush=True)
     case = inputs.make_case(wl, args.seed, pad="finite")
