@@ -17,6 +17,21 @@ topological order, parent[i] in [-1, i-1], -1 = hanging off the committed prefix
   * the committed path runs from the root to the deepest accepted node (smallest node index among
     equally deep ones); the correction token is g at that node's row, or g[0] if none is accepted.
 
+Tree speculative sampling (textbook page, "Faster decoding", section on modified rejection sampling
+keeping the target distribution): at one position a candidate X drawn from the candidate
+distribution q is accepted with probability a(v) = min(1, p(v) / q(v)); on rejection the emitted
+token is drawn from the residual r = [p - q]_+ / Z, Z = sum_u [p - q]_+ (the rejection
+probability; Z = 0 means nothing is ever rejected). The pages apply this left to right along a
+chain, stop at the first rejection with a correction token, and draw a bonus token from the
+target's next distribution when every candidate is accepted. Tree reading (the pages give no
+tree rule): the children of a position are candidates drawn independently from that position's
+q and are tried in index order; after a rejection the residual takes the place of p for the next
+child (the same identity applied again), so a chain is exactly the pages' rule. All children
+rejected: the correction token is drawn from the last residual; an accepted node without
+children ends the path with a bonus token drawn from its row's p. Randomness comes in as
+uniforms in [0, 1): u_accept per node, u_sample per sequence; accept iff u < a, and a token is
+drawn from weights w as the smallest index whose running sum of w exceeds u * sum(w).
+
 Commit (textbook page, "Faster decoding", reserve / execute / commit: after verification only the
 target KV of the accepted draft prefix is committed; rejected branches are released, and the
 correction token's KV is produced by the next round): the K/V rows of the path's nodes are copied,
@@ -82,6 +97,67 @@ def greedy_accept(logits: np.ndarray, draft: np.ndarray, parent: np.ndarray, dty
         path[b, :len(chain)] = chain
         nxt[b] = g[b, best + 1]
     return g, acc_len, path, nxt
+
+
+def sample_index(w: np.ndarray, u: float) -> int:
+    """The smallest index whose running sum of the non-negative weights w exceeds u * sum(w); if
+    rounding leaves none, the last index with positive weight (0 if there is none)."""
+    w = np.asarray(w, dtype=np.float64)
+    c = np.cumsum(w)
+    hit = np.nonzero(c > u * c[-1])[0]
+    if hit.size:
+        return int(hit[0])
+    pos = np.nonzero(w > 0)[0]
+    return int(pos[-1]) if pos.size else 0
+
+
+def spec_sample(p: np.ndarray, q: np.ndarray, draft: np.ndarray, parent: np.ndarray,
+                u_accept: np.ndarray, u_sample: np.ndarray):
+    """p, q: float32 [B, T + 1, V] target and candidate distributions (row 0 at the last
+    committed token, row i + 1 at tree node i: the distributions of the next token there);
+    draft / parent int32 [B, T]; u_accept float64 [B, T]; u_sample float64 [B].
+
+    Returns (accept_len [B], path [B, T] (root first, -1 past the end), next_token [B])."""
+    B, T = draft.shape
+    acc_len = np.zeros(B, np.int32)
+    path = np.full((B, T), -1, np.int32)
+    nxt = np.zeros(B, np.int32)
+    for b in range(B):
+        kids = [[] for _ in range(T + 1)]          # kids[pos + 1]: children of pos, index order
+        for i in range(T):
+            pa = int(parent[b, i])
+            if pa < -1 or pa >= i:
+                raise ValueError(f"parent[{b}][{i}] = {pa} is not in [-1, {i - 1}]")
+            kids[pa + 1].append(i)
+        chain, pos = [], -1
+        while True:
+            row = pos + 1
+            target = p[b, row].astype(np.float64)  # the pages' p at this position
+            cand = q[b, row].astype(np.float64)    # the pages' q
+            taken = None
+            for c in kids[row]:
+                x = int(draft[b, c])
+                excess = np.maximum(target - cand, 0.0)
+                Z = excess.sum()
+                if Z == 0.0:
+                    a = 1.0                        # no rejection is possible
+                elif cand[x] > 0.0:
+                    a = min(1.0, target[x] / cand[x])
+                else:
+                    a = 1.0 if target[x] > 0.0 else 0.0
+                if u_accept[b, c] < a:
+                    taken = c
+                    break
+                target = excess / Z                # the residual r replaces p for the next child
+            if taken is None:
+                # every child rejected: correction from the last residual; no child: bonus from p
+                nxt[b] = sample_index(target, float(u_sample[b]))
+                break
+            chain.append(taken)
+            pos = taken
+        acc_len[b] = len(chain)
+        path[b, :len(chain)] = chain
+    return acc_len, path, nxt
 
 
 def commit_kv(k_cache, v_cache, seq_lens, k_tree, v_tree, path, accept_len, *, block_table=None,

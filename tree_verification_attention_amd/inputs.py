@@ -404,3 +404,63 @@ def random_paths(parent: np.ndarray, rng: np.random.Generator, max_len=None):
         path[b, :len(chain)] = chain
         n[b] = len(chain)
     return path, n
+
+
+@dataclasses.dataclass
+class SpecCase:
+    """Operands of tree speculative sampling: target and candidate distributions p, q float32
+    [B, T + 1, V] (row 0 = the position after the last committed token, row i + 1 = after tree
+    node i), draft tokens and parent arrays int32 [B, T], uniforms u_accept float64 [B, T] and
+    u_sample float64 [B]."""
+
+    p: np.ndarray
+    q: np.ndarray
+    draft: np.ndarray
+    parent: np.ndarray
+    u_accept: np.ndarray
+    u_sample: np.ndarray
+
+
+def _softmax_rows(z: np.ndarray) -> np.ndarray:
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z, dtype=np.float64)
+    return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def make_spec_case(B: int, T: int, V: int, seed: int = 0, *, tree: str = "bounded",
+                   mode: str = "overlap", sharp: float = 2.5, noise: float = 1.0,
+                   depth_cap: int = 8, branch_cap: int = 4) -> SpecCase:
+    """Target rows p = softmax(N(0, sharp^2) logits); candidate rows q = softmax of the same
+    logits plus N(0, noise^2) (partial overlap). ``mode`` "same": q = p; "disjoint": p keeps only
+    the odd tokens and q only the even ones (renormalised). The children of every position are
+    drawn independently from that position's q row (inverse CDF of a seeded uniform), as a
+    drafter sampling them would. Uniforms are seeded float64 in [0, 1)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 11]))
+    wl = Workload("spec", B=B, Hq=1, Hkv=1, D=64, T=T, L=0, tree=tree, depth_cap=depth_cap,
+                  branch_cap=branch_cap)
+    parent = np.stack([make_tree(rng, wl) for _ in range(B)]).astype(np.int32)
+    p = np.empty((B, T + 1, V), np.float32)
+    q = np.empty((B, T + 1, V), np.float32)
+    for b in range(B):
+        z = rng.standard_normal((T + 1, V), dtype=np.float32) * np.float32(sharp)
+        p[b] = _softmax_rows(z)
+        if mode == "same":
+            q[b] = p[b]
+        elif mode == "disjoint":
+            mask = (np.arange(V) % 2).astype(np.float32)
+            pp = p[b] * mask
+            qq = _softmax_rows(z) * (1.0 - mask)
+            p[b] = (pp / pp.sum(axis=-1, keepdims=True)).astype(np.float32)
+            q[b] = (qq / qq.sum(axis=-1, keepdims=True)).astype(np.float32)
+        else:
+            q[b] = _softmax_rows(z + rng.standard_normal((T + 1, V), dtype=np.float32)
+                                 * np.float32(noise))
+    draft = np.zeros((B, T), np.int32)
+    for b in range(B):
+        for i in range(T):
+            row = q[b, int(parent[b, i]) + 1].astype(np.float64)
+            c = np.cumsum(row)
+            draft[b, i] = min(int(np.searchsorted(c, rng.random() * c[-1], side="right")), V - 1)
+    u_accept = rng.random((B, T))
+    u_sample = rng.random(B)
+    return SpecCase(p=p, q=q, draft=draft, parent=parent, u_accept=u_accept, u_sample=u_sample)
