@@ -217,6 +217,23 @@ def time_next_rows(steps, warmup, seed):
     del lg
     torch.cuda.empty_cache()
 
+    print("[bench] tree speculative sampling", file=sys.stderr, flush=True)
+    sc = inputs.make_spec_case(B, T, V, seed)
+    sp, sq = torch.from_numpy(sc.p).cuda(), torch.from_numpy(sc.q).cuda()
+    sd, spa = torch.from_numpy(sc.draft).cuda(), torch.from_numpy(sc.parent).cuda()
+    sua, sus = torch.from_numpy(sc.u_accept).cuda(), torch.from_numpy(sc.u_sample).cuda()
+    sws = torch.empty(_lib.spec_sample_workspace_size(B, T, V), dtype=torch.uint8, device="cuda")
+    spec_us = timed(lambda: _lib.spec_sample(sp, sq, sd, spa, sua, sus, ws=sws))
+    s_n, _, _ = _lib.spec_sample(sp, sq, sd, spa, sua, sus, ws=sws)
+    # the mass kernel reads p of every row and q of every row whose position has children
+    internal = sum(len(set(int(x) for x in sc.parent[b])) for b in range(B))
+    spec_bytes = 4 * V * (B * (T + 1) + internal)
+    t0 = time.perf_counter()
+    oacc.spec_sample(sc.p, sc.q, sc.draft, sc.parent, sc.u_accept, sc.u_sample)
+    spec_cpu_s = time.perf_counter() - t0
+    del sp, sq
+    torch.cuda.empty_cache()
+
     wl = inputs.Workload("commit", B=B, Hq=32, Hkv=8, D=128, T=T, L=4096)
     cc = inputs.make_case(wl, seed, pad="finite", lcap=4096 + T)
     dv = lambda a: (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
@@ -237,6 +254,14 @@ def time_next_rows(steps, warmup, seed):
             "frac": round(acc_bytes / (acc_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "mean_accept_len": float(n_gpu.float().mean().item()),
             "cpu_oracle_s": round(cpu_s, 3)},
+        "spec_sample": {
+            "workload": f"B={B}, T={T} bounded tree, vocab {V}, fp32 p and q",
+            "us": round(spec_us, 2), "mass_kernel_bytes": spec_bytes,
+            "achieved_gbs": round(spec_bytes / (spec_us * 1e-6) / 1e9, 1),
+            "peak_gbs": HBM_PEAK_GBS,
+            "frac": round(spec_bytes / (spec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "mean_accept_len": float(s_n.float().mean().item()),
+            "cpu_oracle_s": round(spec_cpu_s, 3)},
         "kv_commit": {
             "workload": f"B={B}, Hkv=8, D=128 bf16, contiguous cache, {int(n.sum())} rows committed",
             "us": round(com_us, 2), "algorithmic_bytes": com_bytes,
@@ -380,7 +405,8 @@ def accept_stats_summary(stats_dir, steps):
         raise SystemExit(f"no kernel stats under {stats_dir}")
     with open(paths[0]) as f:
         stats = list(csv.DictReader(f))
-    names = ("argmax_kernel", "accept_kernel", "commit_kernel", "lens_kernel")
+    names = ("argmax_kernel", "accept_kernel", "spec_mass_kernel", "spec_walk_kernel",
+             "commit_kernel", "lens_kernel")
     rows = [r for r in stats if any(n in r["Name"] for n in names)]
     bench = None
     logs = glob.glob(stats_dir.rstrip("/") + ".log")
@@ -391,7 +417,8 @@ def accept_stats_summary(stats_dir, steps):
     out = os.path.join(PROFILES, "argmax_kernel_greedy_accept_b4_t64_v128256_stats.txt")
     lines = [
         "# rocprofv3 kernel statistics, greedy tree acceptance (B=4, T=64, vocab 128256, bf16 "
-        "logits) and accepted-path KV commit (B=4, Hkv=8, D=128 bf16)",
+        "logits), tree speculative sampling (same tree and vocabulary, fp32 p and q) and "
+        "accepted-path KV commit (B=4, Hkv=8, D=128 bf16)",
         f"# command: rocprofv3 --kernel-trace --stats -d STATS_DIR -o run --output-format csv -- "
         f"python3 bench.py --next-rows-only --steps {steps} --warmup 5",
         f"# summary: python3 bench.py --steps {steps} --accept-stats-summary STATS_DIR",

@@ -58,9 +58,11 @@ typedef enum ta_dtype {
 #define TA_DEV_BAD_LEN 2u      /* seq_lens[b] outside [0, capacity] */
 #define TA_DEV_BAD_PAGE 4u     /* a block-table entry used by a prefix outside [0, num_pages) */
 #define TA_DEV_BAD_COMMIT 8u   /* a commit past the cache capacity, or a path entry outside [0, T) */
+#define TA_DEV_BAD_TOKEN 16u   /* a draft token outside [0, V) (speculative sampling rejects it) */
 
 /* Largest tree the kernels accept. */
 #define TA_MAX_TREE 256
+#define TA_MAX_VOCAB (1 << 20) /* largest vocabulary tree_spec_sample accepts */
 
 /*
  * One attention layer of a verify step. Plain C struct, read during the call only.
@@ -221,6 +223,40 @@ int tree_greedy_accept(const void *logits, int dtype, int64_t row_stride, int B,
 
 /* Host-only. Workspace bytes tree_greedy_accept needs for these sizes on the current device. */
 int tree_greedy_accept_workspace_size(int dtype, int B, int T, int V, size_t *bytes);
+
+/*
+ * Tree speculative sampling (textbook page, "Faster decoding", section on modified rejection
+ * sampling keeping the target distribution). At a position, a candidate x drawn from q is accepted
+ * with probability min(1, p(x) / q(x)); a rejection draws from the residual [p - q]_+ / Z, and
+ * Z = 0 means no rejection happens. The pages state this along a chain; on a tree the children of
+ * a position are candidates drawn independently from its q, tried in index order, and after each
+ * rejection the residual stands in for p when the next child is tried (a chain is the pages'
+ * rule). With every child of a position rejected, the correction token is drawn from the last
+ * residual; an accepted node without children ends the path with a bonus token drawn from its
+ * row's p. "Drawn from weights w with uniform u" means: the smallest index whose running sum of w
+ * exceeds u * sum(w) (if rounding leaves none, the last index with positive weight).
+ *   p, q        float32 [B, T + 1, V]: target and candidate distributions of the next token at
+ *               the last committed token (row 0) and after tree node i (row i + 1); consecutive
+ *               rows ``row_stride`` elements (>= V) apart, base and rows 16-byte aligned.
+ *   draft       int32 [B, T]: the candidate token of every node (drawn from q at its parent's row).
+ *   parent      int32 [B, T]: topological parent array (-1 = attached to the committed prefix).
+ *   u_accept    float64 [B, T]: uniform in [0, 1) per node (accept iff u < the acceptance
+ *               probability); u_sample float64 [B]: uniform for the emitted token.
+ * Outputs (device memory, caller-owned): accept_len int32 [B]; path int32 [B, T] (accepted
+ * nodes, root first, -1 past accept_len); next_token int32 [B] (correction or bonus token).
+ * All sums are fp64 over the fp32 inputs. ``ws``: device memory of at least
+ * tree_spec_sample_workspace_size() bytes, 256-byte aligned. Parents outside [-1, i-1] set
+ * TA_DEV_BAD_PARENT and count as -1; draft tokens outside [0, V) set TA_DEV_BAD_TOKEN and are
+ * treated as tokens of zero target mass. 0 <= B <= 65535, 1 <= T <= TA_MAX_TREE,
+ * 1 <= V <= TA_MAX_VOCAB.
+ */
+int tree_spec_sample(const float *p, const float *q, int64_t row_stride, int B, int T, int V,
+                     const int32_t *draft, const int32_t *parent, const double *u_accept,
+                     const double *u_sample, void *ws, size_t ws_bytes, int32_t *accept_len,
+                     int32_t *path, int32_t *next_token, int32_t *err_flag, hipStream_t stream);
+
+/* Host-only. Workspace bytes tree_spec_sample needs: B * (T + 1) * ceil(V / 4096) doubles. */
+int tree_spec_sample_workspace_size(int B, int T, int V, size_t *bytes);
 
 /*
  * Accepted-path KV commit (textbook page, "Faster decoding", reserve / execute / commit: only

@@ -129,6 +129,8 @@ def spec_sample(p: np.ndarray, q: np.ndarray, draft: np.ndarray, parent: np.ndar
             if pa < -1 or pa >= i:
                 raise ValueError(f"parent[{b}][{i}] = {pa} is not in [-1, {i - 1}]")
             kids[pa + 1].append(i)
+            if not 0 <= int(draft[b, i]) < p.shape[2]:
+                raise ValueError(f"draft[{b}][{i}] = {int(draft[b, i])} is outside the vocabulary")
         chain, pos = [], -1
         while True:
             row = pos + 1

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libtreeattn.so")
 
 TA_OK, TA_EINVAL, TA_EUNSUPPORTED, TA_EWORKSPACE, TA_EHIP = range(5)
 TA_BF16, TA_F32 = 0, 1
-TA_DEV_BAD_PARENT, TA_DEV_BAD_LEN, TA_DEV_BAD_PAGE, TA_DEV_BAD_COMMIT = 1, 2, 4, 8
+TA_DEV_BAD_PARENT, TA_DEV_BAD_LEN, TA_DEV_BAD_PAGE, TA_DEV_BAD_COMMIT, TA_DEV_BAD_TOKEN = 1, 2, 4, 8, 16
 TA_MAX_TREE = 256
 
 # Functions the header declares (checked against the shared object by the test suite).
@@ -26,7 +26,8 @@ EXPORTS = ("tree_mask_build", "tree_attn_workspace_size", "tree_attn_num_splits"
            "tree_attn_prefix", "tree_attn_tree", "tree_attn_merge", "tree_attn_forward",
            "tree_attn_partials", "tree_attn_combine", "tree_attn_workspace_lse_offset",
            "tree_attn_status_string", "tree_attn_abi_version", "tree_greedy_accept",
-           "tree_greedy_accept_workspace_size",
+           "tree_greedy_accept_workspace_size", "tree_spec_sample",
+           "tree_spec_sample_workspace_size",
            "tree_kv_commit")
 
 
@@ -85,6 +86,8 @@ def load(path: str = LIB_PATH):
     lib.tree_attn_abi_version.argtypes = []
     lib.tree_greedy_accept.argtypes = [P, I, ctypes.c_int64, I, I, I, P, P, P, S, P, P, P, P, P, P]
     lib.tree_greedy_accept_workspace_size.argtypes = [I, I, I, I, ctypes.POINTER(S)]
+    lib.tree_spec_sample.argtypes = [P, P, ctypes.c_int64, I, I, I, P, P, P, P, P, S, P, P, P, P, P]
+    lib.tree_spec_sample_workspace_size.argtypes = [I, I, I, ctypes.POINTER(S)]
     lib.tree_kv_commit.argtypes = [PP, P, P, P, P, P, P, P]
     for fn in EXPORTS:
         if fn not in ("tree_attn_status_string",):
@@ -312,6 +315,41 @@ def greedy_accept(logits, draft, parent, *, ws=None, err=None):
         ws.numel() * ws.element_size(), greedy.data_ptr(), n.data_ptr(), path.data_ptr(),
         nxt.data_ptr(), _gpu(err, "err", torch.int32), _stream()))
     return greedy, n, path, nxt
+
+
+def spec_sample_workspace_size(B: int, T: int, V: int) -> int:
+    """Workspace bytes (at least 256) that spec_sample needs for these sizes."""
+    need = ctypes.c_size_t(0)
+    _check("tree_spec_sample_workspace_size",
+           load().tree_spec_sample_workspace_size(B, T, V, ctypes.byref(need)))
+    return max(need.value, 256)
+
+
+def spec_sample(p, q, draft, parent, u_accept, u_sample, *, ws=None, err=None):
+    """Tree speculative sampling. p, q float32 [B, T + 1, V] (same row stride, contiguous last
+    dimension); draft / parent int32 [B, T]; u_accept float64 [B, T]; u_sample float64 [B]
+    -> (accept_len [B], path [B, T], next_token [B]), all int32."""
+    for name, t in (("p", p), ("q", q)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+        if t.stride(-1) != 1 or t.stride(0) != t.shape[1] * t.stride(1):
+            raise ValueError(f"{name} rows must be evenly strided with a contiguous last dimension")
+    if p.shape != q.shape or p.stride() != q.stride():
+        raise ValueError("p and q must have the same shape and strides")
+    B, T1, V = p.shape
+    T = T1 - 1
+    dev = p.device
+    if ws is None:
+        ws = torch.empty(spec_sample_workspace_size(B, T, V), dtype=torch.uint8, device=dev)
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty((B, T), dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    _check("tree_spec_sample", load().tree_spec_sample(
+        _gpu(p, "p"), _gpu(q, "q"), p.stride(1), B, T, V, _gpu(draft, "draft", torch.int32),
+        _gpu(parent, "parent", torch.int32), _gpu(u_accept, "u_accept", torch.float64),
+        _gpu(u_sample, "u_sample", torch.float64), _gpu(ws, "ws"), ws.numel() * ws.element_size(),
+        n.data_ptr(), path.data_ptr(), nxt.data_ptr(), _gpu(err, "err", torch.int32), _stream()))
+    return n, path, nxt
 
 
 def kv_commit(k_cache, v_cache, seq_lens, k_tree, v_tree, path, accept_len, *, block_table=None,

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libtreeattn.so")
-SOURCES = ["abi.cpp", "attn_prefix.hip", "attn_tree.hip", "attn_f32.hip", "mask_merge.hip", "accept.hip"]
+SOURCES = ["abi.cpp", "attn_prefix.hip", "attn_tree.hip", "attn_f32.hip", "mask_merge.hip", "accept.hip",
+           "spec.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -390,6 +390,39 @@ int tree_greedy_accept(const void *logits, int dtype, int64_t row_stride, int B,
                                            path, next_token, err_flag, stream));
 }
 
+static int check_spec(int B, int T, int V) {
+    if (B < 0 || B > 65535 || T < 1 || T > TA_MAX_TREE || V < 1 || V > TA_MAX_VOCAB)
+        return TA_EINVAL;
+    return TA_OK;
+}
+
+int tree_spec_sample_workspace_size(int B, int T, int V, size_t *bytes) {
+    int rc = check_spec(B, T, V);
+    if (rc) return rc;
+    if (!bytes) return TA_EINVAL;
+    *bytes = align256((size_t)B * (T + 1) * ta::spec_sample_chunks(V) * sizeof(double));
+    return TA_OK;
+}
+
+int tree_spec_sample(const float *p, const float *q, int64_t row_stride, int B, int T, int V,
+                     const int32_t *draft, const int32_t *parent, const double *u_accept,
+                     const double *u_sample, void *ws, size_t ws_bytes, int32_t *accept_len,
+                     int32_t *path, int32_t *next_token, int32_t *err_flag, hipStream_t stream) {
+    int rc = check_spec(B, T, V);
+    if (rc) return rc;
+    if (row_stride < V || (row_stride * 4) % 16) return TA_EINVAL;
+    if (B == 0) return TA_OK;
+    if (!p || !q || !draft || !parent || !u_accept || !u_sample || !accept_len || !path ||
+        !next_token)
+        return TA_EINVAL;
+    if (!aligned16(p) || !aligned16(q)) return TA_EINVAL;
+    const size_t need = (size_t)B * (T + 1) * ta::spec_sample_chunks(V) * sizeof(double);
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) return TA_EWORKSPACE;
+    ta::SpecArgs a{p, q, row_stride, B, T, V, draft, parent, u_accept, u_sample,
+                   static_cast<double *>(ws), accept_len, path, next_token, err_flag};
+    return status(ta::launch_spec_sample(a, stream));
+}
+
 int tree_kv_commit(const ta_problem *p, void *k_cache, void *v_cache, const int32_t *path,
                    const int32_t *accept_len, int32_t *new_seq_lens, int32_t *err_flag,
                    hipStream_t stream) {

@@ -78,6 +78,21 @@ hipError_t launch_attn_prefix(const AttnArgs &a, int nw, hipStream_t s);
 hipError_t launch_attn_tree(const AttnArgs &a, int nw, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &m, bool out_bf16, hipStream_t s);
+struct SpecArgs {
+    const float *p, *q;      // [B, T + 1, V] target / candidate distributions, row_stride apart
+    int64_t row_stride;      // elements
+    int B, T, V;
+    const int32_t *draft, *parent;
+    const double *u_accept;  // [B, T]
+    const double *u_sample;  // [B]
+    double *sums;            // workspace: [B * (T + 1)][spec_sample_chunks(V)] chunk sums
+    int32_t *accept_len, *path, *next_token, *err;
+};
+
+// 4096-entry chunks per row of tree speculative sampling.
+int spec_sample_chunks(int V);
+hipError_t launch_spec_sample(const SpecArgs &a, hipStream_t s);
+
 // Chunks per logits row for the argmax (the workspace holds B * (T + 1) * chunks int2 winners).
 int greedy_accept_chunks(int V, bool bf16);
 hipError_t launch_greedy_accept(const void *logits, bool bf16, int64_t row_stride, int B, int T,
