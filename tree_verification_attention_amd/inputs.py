@@ -464,3 +464,44 @@ def make_spec_case(B: int, T: int, V: int, seed: int = 0, *, tree: str = "bounde
     u_accept = rng.random((B, T))
     u_sample = rng.random(B)
     return SpecCase(p=p, q=q, draft=draft, parent=parent, u_accept=u_accept, u_sample=u_sample)
+
+
+@dataclasses.dataclass
+class GdnCase:
+    """Operands of one gated-delta-net layer's tree verification: q, k [B, T, H_k, d_k] and v
+    [B, T, H_v, d_v] (bf16 bits), log-decays g and write strengths beta fp32 [B, T, H_v], parent
+    int32 [B, T], committed states S0 fp32 [B, H_v, d_k, d_v], output scale."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    beta: np.ndarray
+    parent: np.ndarray
+    S0: np.ndarray
+    scale: float
+
+
+def make_gdn_case(B: int, T: int, Hk: int = 16, Hv: int = 32, dk: int = 128, dv: int = 128,
+                  seed: int = 0, *, tree: str = "bounded", depth_cap: int = 8,
+                  branch_cap: int = 4) -> GdnCase:
+    """q and k N(0, 1) rows scaled to unit length (as the layer's L2 normalisation does) and
+    rounded to bf16; v N(0, 1) in bf16; g uniform in [-0.2, -0.01] (alpha = e^g in about
+    [0.82, 0.99]); beta uniform in [0.05, 0.95]; S0 N(0, 0.05^2); scale 1 / sqrt(d_k)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 13]))
+    wl = Workload("gdn", B=B, Hq=1, Hkv=1, D=64, T=T, L=0, tree=tree, depth_cap=depth_cap,
+                  branch_cap=branch_cap)
+    parent = np.stack([make_tree(rng, wl) for _ in range(B)]).astype(np.int32)
+
+    def unit(shape):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        x /= np.linalg.norm(x, axis=-1, keepdims=True)
+        return f32_to_bf16_bits(x)
+
+    q = unit((B, T, Hk, dk))
+    k = unit((B, T, Hk, dk))
+    v = f32_to_bf16_bits(rng.standard_normal((B, T, Hv, dv), dtype=np.float32))
+    g = rng.uniform(-0.2, -0.01, (B, T, Hv)).astype(np.float32)
+    beta = rng.uniform(0.05, 0.95, (B, T, Hv)).astype(np.float32)
+    S0 = (rng.standard_normal((B, Hv, dk, dv), dtype=np.float32) * np.float32(0.05))
+    return GdnCase(q=q, k=k, v=v, g=g, beta=beta, parent=parent, S0=S0, scale=float(dk) ** -0.5)
