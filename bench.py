@@ -234,6 +234,31 @@ def time_next_rows(steps, warmup, seed):
     del sp, sq
     torch.cuda.empty_cache()
 
+    print("[bench] GDN tree verification", file=sys.stderr, flush=True)
+    import oracle.gdn as ogdn
+    GT, GHk, GHv, Gd = 128, 16, 32, 128
+    gc = inputs.make_gdn_case(B, GT, GHk, GHv, Gd, Gd, seed)
+    bt = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    gq, gk, gv = bt(gc.q), bt(gc.k), bt(gc.v)
+    gg, gb = torch.from_numpy(gc.g).cuda(), torch.from_numpy(gc.beta).cuda()
+    gp, gs0 = torch.from_numpy(gc.parent).cuda(), torch.from_numpy(gc.S0).cuda()
+    gdn_us = timed(lambda: _lib.gdn_verify(gq, gk, gv, gg, gb, gp, gs0, gc.scale))
+    # algorithmic work: K S0 and Q S0 (2 T dk dv each), and per node and ancestor-or-self pair
+    # the two key dot products (2 dk each) and the rank-1 terms (2 dv each)
+    pairs = 0
+    for b in range(B):
+        for t in range(GT):
+            j = t
+            while j >= 0:
+                pairs += 1
+                j = int(gc.parent[b, j])
+    gdn_flops = GHv * (B * 4 * GT * Gd * Gd + pairs * (4 * Gd + 4 * Gd))
+    gdn_bytes = (gc.q.nbytes + gc.k.nbytes + gc.v.nbytes + gc.g.nbytes + gc.beta.nbytes
+                 + gc.parent.nbytes + gc.S0.nbytes + B * GT * GHv * Gd * 4)
+    t0 = time.perf_counter()
+    ogdn.gdn_tree_verify(gc.q, gc.k, gc.v, gc.g, gc.beta, gc.parent, gc.S0, gc.scale)
+    gdn_cpu_s = time.perf_counter() - t0
+
     wl = inputs.Workload("commit", B=B, Hq=32, Hkv=8, D=128, T=T, L=4096)
     cc = inputs.make_case(wl, seed, pad="finite", lcap=4096 + T)
     dv = lambda a: (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
@@ -262,6 +287,14 @@ def time_next_rows(steps, warmup, seed):
             "frac": round(spec_bytes / (spec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "mean_accept_len": float(s_n.float().mean().item()),
             "cpu_oracle_s": round(spec_cpu_s, 3)},
+        "gdn_verify": {
+            "workload": f"B={B}, T={GT} bounded tree, H_k={GHk}, H_v={GHv}, d_k=d_v={Gd}, "
+                        "bf16 q/k/v, fp32 states",
+            "us": round(gdn_us, 2), "algorithmic_flops": gdn_flops,
+            "achieved_tflops": round(gdn_flops / (gdn_us * 1e-6) / 1e12, 2),
+            "peak_tflops": 157.3, "bound": "alu (fp32)",
+            "frac": round(gdn_flops / (gdn_us * 1e-6) / 1e12 / 157.3, 4),
+            "bytes": gdn_bytes, "cpu_oracle_s": round(gdn_cpu_s, 3)},
         "kv_commit": {
             "workload": f"B={B}, Hkv=8, D=128 bf16, contiguous cache, {int(n.sum())} rows committed",
             "us": round(com_us, 2), "algorithmic_bytes": com_bytes,
@@ -406,7 +439,7 @@ def accept_stats_summary(stats_dir, steps):
     with open(paths[0]) as f:
         stats = list(csv.DictReader(f))
     names = ("argmax_kernel", "accept_kernel", "spec_mass_kernel", "spec_walk_kernel",
-             "commit_kernel", "lens_kernel")
+             "gdn_verify_kernel", "commit_kernel", "lens_kernel")
     rows = [r for r in stats if any(n in r["Name"] for n in names)]
     bench = None
     logs = glob.glob(stats_dir.rstrip("/") + ".log")

@@ -259,6 +259,42 @@ int tree_spec_sample(const float *p, const float *q, int64_t row_stride, int B, 
 int tree_spec_sample_workspace_size(int B, int T, int V, size_t *bytes);
 
 /*
+ * Tree verification of a gated-delta-net (GDN) layer (DFlash-TfM summary page, "Rollback-free
+ * tree verification for GDN"). The layer keeps a d_k x d_v state per value head and updates it
+ * per token as S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T, alpha_t = e^{g_t};
+ * on the tree every node continues its parent's state (root-attached nodes continue S0) and the
+ * output is o_t = scale * S_t^T q_t. Computed without forming any node state: the pseudo-values U
+ * solve the lower-triangular system (I + X) U = beta (V - e^{G} K S0) over the ancestor structure
+ * (X_tj = beta_t e^{G_t - G_j} k_t.k_j for strict ancestors j, G = log-decay summed over the path),
+ * then o_t = scale (e^{G_t} S0^T q_t + sum over ancestors-or-self j of e^{G_t - G_j} (q_t.k_j) u_j).
+ *   q, k        bf16 [B, T, Hk, dk] (contiguous); v bf16 [B, T, Hv, dv]; value head h reads key
+ *               head h / (Hv / Hk).
+ *   g, beta     float32 [B, T, Hv]: log-decay (<= 0) and write strength of every node and head.
+ *   parent      int32 [B, T] topological parent array (-1 = attached to the committed state).
+ *   S0          float32 [B, Hv, dk, dv]: the committed states (read only).
+ *   o           float32 [B, T, Hv, dv] (caller-owned device memory).
+ * dk in {64, 128}; dv a multiple of 32, at most 256; Hv a multiple of Hk; 1 <= T <= TA_MAX_TREE;
+ * every pointer 16-byte aligned. Parents outside [-1, i-1] set TA_DEV_BAD_PARENT and count as -1.
+ */
+int tree_gdn_verify(const void *q, const void *k, const void *v, const float *g,
+                    const float *beta, const int32_t *parent, const float *S0, int B, int T,
+                    int Hk, int Hv, int dk, int dv, float scale, float *o, int32_t *err_flag,
+                    hipStream_t stream);
+
+/*
+ * The deferred state commit of a GDN layer (same page: the state is committed in the next
+ * iteration, once the accepted branch is known, so nothing is rolled back): for every sequence b
+ * and value head, S[b] becomes the state after the updates of path[b][0 .. accept_len[b] - 1]
+ * (root first, as greedy acceptance or speculative sampling return it), i.e. the state of the
+ * last accepted node. S: float32 [B, Hv, dk, dv], updated in place; k, v, g, beta as in
+ * tree_gdn_verify. accept_len outside [0, T] leaves S[b] unchanged, a path entry outside [0, T)
+ * stops the sequence's updates there; both set TA_DEV_BAD_COMMIT.
+ */
+int tree_gdn_commit(const void *k, const void *v, const float *g, const float *beta, int B,
+                    int T, int Hk, int Hv, int dk, int dv, const int32_t *path,
+                    const int32_t *accept_len, float *S, int32_t *err_flag, hipStream_t stream);
+
+/*
  * Accepted-path KV commit (textbook page, "Faster decoding", reserve / execute / commit: only
  * the accepted draft prefix's target KV is committed, rejected branches are released). For every
  * sequence b, the tree K/V rows path[b][j], j < accept_len[b], are copied to cache positions

@@ -27,7 +27,7 @@ EXPORTS = ("tree_mask_build", "tree_attn_workspace_size", "tree_attn_num_splits"
            "tree_attn_partials", "tree_attn_combine", "tree_attn_workspace_lse_offset",
            "tree_attn_status_string", "tree_attn_abi_version", "tree_greedy_accept",
            "tree_greedy_accept_workspace_size", "tree_spec_sample",
-           "tree_spec_sample_workspace_size",
+           "tree_spec_sample_workspace_size", "tree_gdn_verify", "tree_gdn_commit",
            "tree_kv_commit")
 
 
@@ -88,6 +88,8 @@ def load(path: str = LIB_PATH):
     lib.tree_greedy_accept_workspace_size.argtypes = [I, I, I, I, ctypes.POINTER(S)]
     lib.tree_spec_sample.argtypes = [P, P, ctypes.c_int64, I, I, I, P, P, P, P, P, S, P, P, P, P, P]
     lib.tree_spec_sample_workspace_size.argtypes = [I, I, I, ctypes.POINTER(S)]
+    lib.tree_gdn_verify.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, ctypes.c_float, P, P, P]
+    lib.tree_gdn_commit.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, P, P, P]
     lib.tree_kv_commit.argtypes = [PP, P, P, P, P, P, P, P]
     for fn in EXPORTS:
         if fn not in ("tree_attn_status_string",):
@@ -350,6 +352,44 @@ def spec_sample(p, q, draft, parent, u_accept, u_sample, *, ws=None, err=None):
         _gpu(u_sample, "u_sample", torch.float64), _gpu(ws, "ws"), ws.numel() * ws.element_size(),
         n.data_ptr(), path.data_ptr(), nxt.data_ptr(), _gpu(err, "err", torch.int32), _stream()))
     return n, path, nxt
+
+
+def _contig(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d {dtype} tensor")
+    return t.data_ptr()
+
+
+def gdn_verify(q, k, v, g, beta, parent, S0, scale, *, err=None):
+    """Tree verification of a gated-delta-net layer. q, k bf16 [B, T, Hk, dk]; v bf16
+    [B, T, Hv, dv]; g, beta float32 [B, T, Hv]; parent int32 [B, T]; S0 float32
+    [B, Hv, dk, dv] -> o float32 [B, T, Hv, dv]."""
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=q.device)
+    _check("tree_gdn_verify", load().tree_gdn_verify(
+        _contig(q, "q", torch.bfloat16, 4), _contig(k, "k", torch.bfloat16, 4),
+        _contig(v, "v", torch.bfloat16, 4), _contig(g, "g", torch.float32, 3),
+        _contig(beta, "beta", torch.float32, 3), _contig(parent, "parent", torch.int32, 2),
+        _contig(S0, "S0", torch.float32, 4), B, T, Hk, Hv, dk, dv, float(scale), o.data_ptr(),
+        _gpu(err, "err", torch.int32), _stream()))
+    return o
+
+
+def gdn_commit(k, v, g, beta, path, accept_len, S, *, err=None):
+    """Deferred GDN state commit: S (float32 [B, Hv, dk, dv]) becomes, in place, the state after
+    the updates of each sequence's accepted path (int32 [B, T], root first; accept_len int32 [B])."""
+    B, T, Hk, dk = k.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    _check("tree_gdn_commit", load().tree_gdn_commit(
+        _contig(k, "k", torch.bfloat16, 4), _contig(v, "v", torch.bfloat16, 4),
+        _contig(g, "g", torch.float32, 3), _contig(beta, "beta", torch.float32, 3), B, T, Hk, Hv,
+        dk, dv, _contig(path, "path", torch.int32, 2), _contig(accept_len, "accept_len",
+                                                              torch.int32, 1),
+        _contig(S, "S", torch.float32, 4), _gpu(err, "err", torch.int32), _stream()))
+    return S
 
 
 def kv_commit(k_cache, v_cache, seq_lens, k_tree, v_tree, path, accept_len, *, block_table=None,

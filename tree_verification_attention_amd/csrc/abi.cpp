@@ -423,6 +423,41 @@ int tree_spec_sample(const float *p, const float *q, int64_t row_stride, int B, 
     return status(ta::launch_spec_sample(a, stream));
 }
 
+static int check_gdn(int B, int T, int Hk, int Hv, int dk, int dv) {
+    if (dk != 64 && dk != 128) return TA_EUNSUPPORTED;
+    if (dv < 32 || dv > 256 || dv % 32) return TA_EUNSUPPORTED;
+    if (B < 0 || B > 65535 || T < 1 || T > TA_MAX_TREE) return TA_EINVAL;
+    if (Hk < 1 || Hv < 1 || Hv % Hk || Hv > 65535) return TA_EINVAL;
+    return TA_OK;
+}
+
+int tree_gdn_verify(const void *q, const void *k, const void *v, const float *g,
+                    const float *beta, const int32_t *parent, const float *S0, int B, int T,
+                    int Hk, int Hv, int dk, int dv, float scale, float *o, int32_t *err_flag,
+                    hipStream_t stream) {
+    int rc = check_gdn(B, T, Hk, Hv, dk, dv);
+    if (rc) return rc;
+    if (!isfinite(scale)) return TA_EINVAL;
+    if (B == 0) return TA_OK;
+    if (!q || !k || !v || !g || !beta || !parent || !S0 || !o) return TA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S0) || !aligned16(o))
+        return TA_EINVAL;
+    ta::GdnArgs a{q, k, v, g, beta, parent, S0, B, T, Hk, Hv, dk, dv, scale, o, err_flag};
+    return status(ta::launch_gdn_verify(a, stream));
+}
+
+int tree_gdn_commit(const void *k, const void *v, const float *g, const float *beta, int B,
+                    int T, int Hk, int Hv, int dk, int dv, const int32_t *path,
+                    const int32_t *accept_len, float *S, int32_t *err_flag, hipStream_t stream) {
+    int rc = check_gdn(B, T, Hk, Hv, dk, dv);
+    if (rc) return rc;
+    if (B == 0) return TA_OK;
+    if (!k || !v || !g || !beta || !path || !accept_len || !S) return TA_EINVAL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(S)) return TA_EINVAL;
+    ta::GdnCommitArgs a{k, v, g, beta, B, T, Hk, Hv, dk, dv, path, accept_len, S, err_flag};
+    return status(ta::launch_gdn_commit(a, stream));
+}
+
 int tree_kv_commit(const ta_problem *p, void *k_cache, void *v_cache, const int32_t *path,
                    const int32_t *accept_len, int32_t *new_seq_lens, int32_t *err_flag,
                    hipStream_t stream) {

@@ -78,6 +78,29 @@ hipError_t launch_attn_prefix(const AttnArgs &a, int nw, hipStream_t s);
 hipError_t launch_attn_tree(const AttnArgs &a, int nw, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &m, bool out_bf16, hipStream_t s);
+struct GdnArgs {
+    const void *q, *k, *v;   // bf16 [B, T, Hk, dk], [B, T, Hk, dk], [B, T, Hv, dv]
+    const float *g, *beta;   // [B, T, Hv]
+    const int32_t *parent;   // [B, T]
+    const float *S0;         // [B, Hv, dk, dv]
+    int B, T, Hk, Hv, dk, dv;
+    float scale;
+    float *o;                // [B, T, Hv, dv]
+    int32_t *err;
+};
+
+struct GdnCommitArgs {
+    const void *k, *v;       // bf16 [B, T, Hk, dk], [B, T, Hv, dv]
+    const float *g, *beta;   // [B, T, Hv]
+    int B, T, Hk, Hv, dk, dv;
+    const int32_t *path, *accept_len;
+    float *S;                // [B, Hv, dk, dv], updated in place
+    int32_t *err;
+};
+
+hipError_t launch_gdn_verify(const GdnArgs &a, hipStream_t s);
+hipError_t launch_gdn_commit(const GdnCommitArgs &a, hipStream_t s);
+
 struct SpecArgs {
     const float *p, *q;      // [B, T + 1, V] target / candidate distributions, row_stride apart
     int64_t row_stride;      // elements
