@@ -17,9 +17,11 @@
 // their ancestors being done), so no state is ever updated and nothing needs rolling back.
 //
 // gdn_verify_kernel: one 256-thread workgroup per (value-column block of 32, value head,
-//   sequence): K of the head and the S_0 column block in LDS, the pseudo-values U of the block
-//   in LDS (sized for 128 or 256 nodes); each thread owns (node, 16 columns) items. All
-//   arithmetic fp32 (bf16 inputs widened).
+//   sequence). K S_0 and Q S_0 for all nodes run on bf16 MFMA with S_0 split into a high and a
+//   low bf16 part (fp32 accumulation; the split leaves about 2^-16 of S_0's relative precision);
+//   the key dot products of ancestor pairs use the two-term bf16 dot instruction, everything
+//   else is fp32 VALU. K of the head and the pseudo-values U live in LDS (sized for 128 or 256
+//   nodes); in the solve and the output each thread owns (node, 16 columns) items.
 // gdn_commit_kernel: the deferred commit. Once the accepted path is known the committed state
 //   becomes the last accepted node's state, obtained by applying the path's updates to S_0 in
 //   place.
@@ -40,44 +42,37 @@ constexpr int kItemCols = 16;   // columns per (node, half) item
 
 __device__ inline float bf(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// Dot product of two bf16 rows of length DK held in LDS (16-byte aligned).
-template <int DK>
-__device__ inline float dot_lds(const uint16_t *x, const uint16_t *y) {
-    float s = 0.f;
-#pragma unroll 4
-    for (int d = 0; d < DK; d += 8) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(x + d);
-        const uint4 b = *reinterpret_cast<const uint4 *>(y + d);
-        const uint32_t au[4] = {a.x, a.y, a.z, a.w}, bu[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s = fmaf(__uint_as_float(au[e] << 16), __uint_as_float(bu[e] << 16), s);
-            s = fmaf(__uint_as_float(au[e] & 0xffff0000u), __uint_as_float(bu[e] & 0xffff0000u), s);
-        }
-    }
-    return s;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Entry d of a bf16 row held packed in registers (two entries per 32-bit word).
-__device__ inline float unpack(const uint32_t *x, int d) {
-    return __uint_as_float((d & 1) ? (x[d >> 1] & 0xffff0000u) : (x[d >> 1] << 16));
-}
-
-// Dot product of a packed register row (bf16, DK) with a bf16 row in LDS.
+// Dot product of a packed register row (bf16 pairs, DK entries) with a bf16 row in LDS, on the
+// two-term bf16 dot instruction with fp32 accumulation.
 template <int DK>
 __device__ inline float dot_reg_lds(const uint32_t *x, const uint16_t *y) {
-    float s = 0.f;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
 #pragma unroll
     for (int d = 0; d < DK; d += 8) {
         const uint4 b = *reinterpret_cast<const uint4 *>(y + d);
         const uint32_t bu[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s = fmaf(unpack(x, d + 2 * e), __uint_as_float(bu[e] << 16), s);
-            s = fmaf(unpack(x, d + 2 * e + 1), __uint_as_float(bu[e] & 0xffff0000u), s);
-        }
+        for (int e = 0; e < 4; ++e)
+            s[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[d / 2 + e]),
+                                                   __builtin_bit_cast(bf16x2, bu[e]), s[e], false);
     }
-    return s;
+    return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+template <int DK>
+__device__ inline void load_row(uint32_t *x, const uint16_t *src) {
+#pragma unroll
+    for (int d = 0; d < DK; d += 8) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(src + d);
+        x[d / 2] = w.x;
+        x[d / 2 + 1] = w.y;
+        x[d / 2 + 2] = w.z;
+        x[d / 2 + 3] = w.w;
+    }
 }
 
 // Per-tree quantities by pointer jumping in LDS: depth (1 for a root-attached node) and the
@@ -91,25 +86,42 @@ struct TreeLds {
     int32_t max_depth;
 };
 
-__device__ inline int tree_levels(const int32_t *parent, const float *g, const float *beta,
-                                  int64_t gstride, int T, TreeLds &s, int32_t *err) {
+// Thread i's node (T <= kGdnThreads): its parent, log-decay and write strength.
+struct NodeIn {
+    int p;
+    float g, beta;
+};
+
+__device__ inline NodeIn node_in(const int32_t *parent, const float *g, const float *beta,
+                                 int64_t gstride, int T) {
+    const int i = threadIdx.x;
+    if (i >= T) return NodeIn{-1, 0.f, 0.f};
+    return NodeIn{parent[i], g[i * gstride], beta[i * gstride]};
+}
+
+__device__ inline int tree_levels(NodeIn in, int T, TreeLds &s, int32_t *err) {
+    static_assert(TA_MAX_TREE <= kGdnThreads, "one node per thread");
     const int tid = threadIdx.x;
     if (tid == 0) s.max_depth = 0;
-    for (int i = tid; i < T; i += kGdnThreads) {
-        int p = parent[i];
-        if (p < -1 || p >= i) {
+    if (tid < T) {
+        int p = in.p;
+        if (p < -1 || p >= tid) {
             if (err) atomicOr(err, (int32_t)TA_DEV_BAD_PARENT);
             p = -1;
         }
-        s.par[i] = p;
-        s.jmp[0][i] = p;
-        s.dep[0][i] = 1;
-        s.gs[0][i] = g[i * gstride];
-        s.beta[i] = beta[i * gstride];
+        s.par[tid] = p;
+        s.jmp[0][tid] = p;
+        s.dep[0][tid] = 1;
+        s.gs[0][tid] = in.g;
+        s.beta[tid] = in.beta;
     }
     __syncthreads();
     int cur = 0;
     for (int span = 1; span < T; span <<= 1) {
+        // done once every jump pointer has passed the root
+        bool more = false;
+        for (int i = tid; i < T; i += kGdnThreads) more |= s.jmp[cur][i] >= 0;
+        if (!__syncthreads_or(more)) break;
         for (int i = tid; i < T; i += kGdnThreads) {
             const int j = s.jmp[cur][i];
             s.dep[cur ^ 1][i] = s.dep[cur][i] + (j >= 0 ? s.dep[cur][j] : 0);
@@ -119,63 +131,153 @@ __device__ inline int tree_levels(const int32_t *parent, const float *g, const f
         __syncthreads();
         cur ^= 1;
     }
-    for (int i = tid; i < T; i += kGdnThreads) atomicMax(&s.max_depth, s.dep[cur][i]);
+    // the tree's depth: a wavefront maximum, then one LDS atomic per wavefront
+    int md = 0;
+    for (int i = tid; i < T; i += kGdnThreads) md = max(md, s.dep[cur][i]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) md = max(md, __shfl_xor(md, m));
+    if ((tid & 63) == 0) atomicMax(&s.max_depth, md);
     __syncthreads();
     return cur;
 }
 
 template <int DK, int TMAX>
 __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
-    __shared__ __align__(16) float S0b[DK * kColBlock];     // S_0 column block [DK][32]
-    __shared__ __align__(16) float U[TMAX * kColBlock];     // pseudo-values [T][32]
-    __shared__ __align__(16) uint16_t Ks[TMAX * DK];        // keys of the head [T][DK], bf16
+    // keys of the head [T][DK] bf16 and the S_0 column block split into bf16 high and low parts
+    // (S0 = hi + lo to about 2^-16 relative), transposed [32][DK]; rows padded by 16 bytes so
+    // that lanes reading different rows hit different banks
+    constexpr int KS = DK + 8;
+    __shared__ __align__(16) uint16_t Ks[TMAX * KS];
+    __shared__ __align__(16) float U[TMAX * kColBlock];    // pseudo-values [T][32]
+    // coefficients along every node's root path, position m (0 = the node itself, m = its m-th
+    // ancestor j_m): XA = b_t e^{G_t - G_j} (k_t . k_j) for m >= 1, YA = e^{G_t - G_j} (q_t . k_j);
+    // positions past kAncCap are computed where they are used. XA / YA reuse the S_0 halves'
+    // LDS, which is dead once the K S_0 / Q S_0 products are done.
+    constexpr int kAncCap = TMAX <= 128 ? 16 : 8;
+    constexpr int kS0Bytes = 2 * kColBlock * KS * 2, kCoefBytes = 2 * TMAX * kAncCap * 4;
+    __shared__ __align__(16) unsigned char s0buf[kS0Bytes > kCoefBytes ? kS0Bytes : kCoefBytes];
+    uint16_t *S0hi = reinterpret_cast<uint16_t *>(s0buf);
+    uint16_t *S0lo = S0hi + kColBlock * KS;
+    float *XA = reinterpret_cast<float *>(s0buf);
+    float *YA = XA + TMAX * kAncCap;
+    __shared__ int16_t anc[TMAX * kAncCap];  // j_m of every node, -1 past the root
     __shared__ TreeLds tr;
     const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
     const int T = a.T, hk = h / (a.Hv / a.Hk);
     const int c0 = cb * kColBlock;
-    const int lv = tree_levels(a.parent + (int64_t)b * T, a.g + (int64_t)b * T * a.Hv + h,
-                               a.beta + (int64_t)b * T * a.Hv + h, a.Hv, T, tr, a.err);
+    const uint16_t *kg = static_cast<const uint16_t *>(a.k);
+    // every load of a thread is issued before any LDS store, so their latencies overlap
+    constexpr int KV = TMAX * (DK / 8) / kGdnThreads;  // 16-byte key chunks per thread
+    uint4 kc[KV];
+#pragma unroll
+    for (int r = 0; r < KV; ++r) {
+        const int idx = tid + r * kGdnThreads, t = min(idx / (DK / 8), T - 1);
+        kc[r] = *reinterpret_cast<const uint4 *>(
+            kg + (((int64_t)b * T + t) * a.Hk + hk) * DK + (idx % (DK / 8)) * 8);
+    }
+    // S_0 entries (d, c) and (d + 1, c) per thread and step, so that one 32-bit LDS store
+    // takes both of their bf16 parts
+    constexpr int SV = DK * kColBlock / (2 * kGdnThreads);
+    const float *s0 = a.S0 + ((int64_t)b * a.Hv + h) * DK * a.dv;
+    float sx[SV][2];
+#pragma unroll
+    for (int r = 0; r < SV; ++r) {
+        const int idx = tid + r * kGdnThreads, d = 2 * (idx / kColBlock), c = idx % kColBlock;
+        sx[r][0] = s0[(int64_t)d * a.dv + c0 + c];
+        sx[r][1] = s0[(int64_t)(d + 1) * a.dv + c0 + c];
+    }
+    const NodeIn nin = node_in(a.parent + (int64_t)b * T, a.g + (int64_t)b * T * a.Hv + h,
+                               a.beta + (int64_t)b * T * a.Hv + h, a.Hv, T);
+    // keys and S_0 halves into LDS (the loads above are all in flight by now)
+#pragma unroll
+    for (int r = 0; r < KV; ++r) {
+        const int idx = tid + r * kGdnThreads;
+        if (idx / (DK / 8) < T)
+            *reinterpret_cast<uint4 *>(Ks + (idx / (DK / 8)) * KS + (idx % (DK / 8)) * 8) = kc[r];
+    }
+#pragma unroll
+    for (int r = 0; r < SV; ++r) {
+        const int idx = tid + r * kGdnThreads, d = 2 * (idx / kColBlock), c = idx % kColBlock;
+        const __bf16 h0 = (__bf16)sx[r][0], h1 = (__bf16)sx[r][1];
+        const __bf16 l0 = (__bf16)(sx[r][0] - (float)h0), l1 = (__bf16)(sx[r][1] - (float)h1);
+        *reinterpret_cast<bf16x2 *>(S0hi + c * KS + d) = bf16x2{h0, h1};
+        *reinterpret_cast<bf16x2 *>(S0lo + c * KS + d) = bf16x2{l0, l1};
+    }
+    const int lv = tree_levels(nin, T, tr, a.err);
     const int32_t *dep = tr.dep[lv];
     const float *G = tr.gs[lv];
-    // K rows of this key head and the S_0 column block
-    {
-        const uint16_t *kg = static_cast<const uint16_t *>(a.k);
-        for (int idx = tid; idx < T * (DK / 8); idx += kGdnThreads) {
-            const int t = idx / (DK / 8), d8 = idx % (DK / 8);
-            *reinterpret_cast<uint4 *>(Ks + t * DK + d8 * 8) = *reinterpret_cast<const uint4 *>(
-                kg + (((int64_t)b * T + t) * a.Hk + hk) * DK + d8 * 8);
-        }
-        const float *s0 = a.S0 + ((int64_t)b * a.Hv + h) * DK * a.dv;
-        for (int idx = tid; idx < DK * (kColBlock / 4); idx += kGdnThreads) {
-            const int d = idx / (kColBlock / 4), c4 = idx % (kColBlock / 4);
-            *reinterpret_cast<float4 *>(S0b + d * kColBlock + c4 * 4) =
-                *reinterpret_cast<const float4 *>(s0 + (int64_t)d * a.dv + c0 + c4 * 4);
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q);
+    const uint16_t *vg = static_cast<const uint16_t *>(a.v);
+    for (int t = tid; t < T; t += kGdnThreads) {
+        int j = t;
+        for (int m = 0; m < kAncCap; ++m) {
+            anc[t * kAncCap + m] = (int16_t)j;
+            j = j >= 0 ? tr.par[j] : -1;
         }
     }
     __syncthreads();
-    const uint16_t *vg = static_cast<const uint16_t *>(a.v);
-    // right-hand side: w_t = beta_t (v_t - e^{G_t} S_0^T k_t), into U
-    for (int it = tid; it < 2 * T; it += kGdnThreads) {
-        const int t = it >> 1, cc = (it & 1) * kItemCols;
-        float acc[kItemCols];
+    // K S_0 and Q S_0 on v_mfma_f32_32x32x16_bf16, one 32-node tile per wavefront at a time:
+    // lane (l32, hf) supplies node row l32 (A) and value column l32 (B) over k = 16 ks + 8 hf
+    // .. + 7; register r of the result is node 8 (r / 4) + 4 hf + r % 4, column l32
+    for (int nt = wave; nt * 32 < T; nt += kGdnThreads / 64) {
+        // rows past the tree read its last row; their results are dropped below
+        const int row = min(nt * 32 + l32, T - 1);
+        const uint16_t *qrow = qg + (((int64_t)b * T + row) * a.Hk + hk) * DK;
+        bf16x8 aq[DK / 16], ak[DK / 16];
+        float vv[16];
 #pragma unroll
-        for (int c = 0; c < kItemCols; ++c) acc[c] = 0.f;
-        for (int d = 0; d < DK; ++d) {
-            const float kd = bf(Ks[t * DK + d]);
-            const float4 *row = reinterpret_cast<const float4 *>(S0b + d * kColBlock + cc);
+        for (int ks = 0; ks < DK / 16; ++ks)
+            aq[ks] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * ks + 8 * hf);
 #pragma unroll
-            for (int c4 = 0; c4 < kItemCols / 4; ++c4) {
-                const float4 s = row[c4];
-                acc[4 * c4 + 0] = fmaf(kd, s.x, acc[4 * c4 + 0]);
-                acc[4 * c4 + 1] = fmaf(kd, s.y, acc[4 * c4 + 1]);
-                acc[4 * c4 + 2] = fmaf(kd, s.z, acc[4 * c4 + 2]);
-                acc[4 * c4 + 3] = fmaf(kd, s.w, acc[4 * c4 + 3]);
+        for (int r = 0; r < 16; ++r) {
+            const int t = min(nt * 32 + 8 * (r / 4) + 4 * hf + r % 4, T - 1);
+            vv[r] = bf(vg[(((int64_t)b * T + t) * a.Hv + h) * a.dv + c0 + l32]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < DK / 16; ++ks)
+            ak[ks] = *reinterpret_cast<const bf16x8 *>(Ks + row * KS + 16 * ks + 8 * hf);
+        f32x16 accK, accQ;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accK[r] = accQ[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < DK / 16; ++ks) {
+            const int d0 = 16 * ks + 8 * hf;
+            const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(S0hi + l32 * KS + d0);
+            const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(S0lo + l32 * KS + d0);
+            accK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], bh, accK, 0, 0, 0);
+            accK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], bl, accK, 0, 0, 0);
+            accQ = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], bh, accQ, 0, 0, 0);
+            accQ = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], bl, accQ, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = nt * 32 + 8 * (r / 4) + 4 * hf + r % 4;
+            if (t < T) {
+                const float eg = __expf(G[t]);
+                // right-hand side w_t = beta_t (v_t - e^{G_t} S_0^T k_t), into U
+                U[t * kColBlock + l32] = tr.beta[t] * (vv[r] - eg * accK[r]);
+                // e^{G_t} S_0^T q_t goes to the output, which the last phase completes
+                a.o[(((int64_t)b * T + t) * a.Hv + h) * a.dv + c0 + l32] = eg * accQ[r];
             }
         }
-        const float eg = __expf(G[t]), bt = tr.beta[t];
-        const uint16_t *vr = vg + (((int64_t)b * T + t) * a.Hv + h) * a.dv + c0 + cc;
-#pragma unroll
-        for (int c = 0; c < kItemCols; ++c) U[t * kColBlock + cc + c] = bt * (bf(vr[c]) - eg * acc[c]);
+    }
+    __syncthreads();  // the S_0 halves are dead from here on: their LDS takes XA / YA
+    // path coefficients: item (t, half) takes the even or odd positions of t's root path
+    for (int it = tid; it < 2 * T; it += kGdnThreads) {
+        const int t = it >> 1, half = it & 1;
+        if (half >= dep[t]) continue;
+        uint32_t kp[DK / 2], qp[DK / 2];
+        load_row<DK>(qp, qg + (((int64_t)b * T + t) * a.Hk + hk) * DK);
+        load_row<DK>(kp, Ks + t * KS);
+        const float bt = tr.beta[t], gt = G[t];
+        for (int m = half; m < kAncCap; m += 2) {
+            const int j = anc[t * kAncCap + m];
+            if (j < 0) break;
+            const float e = __expf(gt - G[j]);
+            YA[t * kAncCap + m] = e * dot_reg_lds<DK>(qp, Ks + j * KS);
+            if (m > 0) XA[t * kAncCap + m] = bt * e * dot_reg_lds<DK>(kp, Ks + j * KS);
+        }
     }
     __syncthreads();
     // forward substitution, one tree level at a time: u_t -= b_t e^{G_t - G_j} (k_t . k_j) u_j
@@ -188,8 +290,16 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
 #pragma unroll
             for (int c = 0; c < kItemCols; ++c) u[c] = U[t * kColBlock + cc + c];
             const float bt = tr.beta[t], gt = G[t];
-            for (int j = tr.par[t]; j >= 0; j = tr.par[j]) {
-                const float x = bt * __expf(gt - G[j]) * dot_lds<DK>(Ks + t * DK, Ks + j * DK);
+            int m = 1;
+            for (int j = tr.par[t]; j >= 0; j = tr.par[j], ++m) {
+                float x;
+                if (m < kAncCap) {
+                    x = XA[t * kAncCap + m];
+                } else {  // deep paths: the coefficient on the spot
+                    uint32_t kp[DK / 2];
+                    load_row<DK>(kp, Ks + t * KS);
+                    x = bt * __expf(gt - G[j]) * dot_reg_lds<DK>(kp, Ks + j * KS);
+                }
 #pragma unroll
                 for (int c = 0; c < kItemCols; ++c) u[c] = fmaf(-x, U[j * kColBlock + cc + c], u[c]);
             }
@@ -199,44 +309,32 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
         __syncthreads();
     }
     // output: o_t = scale (e^{G_t} S_0^T q_t + sum_{j ancestor or self} e^{G_t - G_j} (q_t . k_j) u_j)
-    const uint16_t *qg = static_cast<const uint16_t *>(a.q);
     for (int it = tid; it < 2 * T; it += kGdnThreads) {
         const int t = it >> 1, cc = (it & 1) * kItemCols;
-        uint32_t qp[DK / 2];  // q_t, bf16 packed in pairs
-        const uint16_t *qr = qg + (((int64_t)b * T + t) * a.Hk + hk) * DK;
-#pragma unroll
-        for (int d = 0; d < DK; d += 8) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(qr + d);
-            qp[d / 2] = w.x;
-            qp[d / 2 + 1] = w.y;
-            qp[d / 2 + 2] = w.z;
-            qp[d / 2 + 3] = w.w;
-        }
+        float *orow = a.o + (((int64_t)b * T + t) * a.Hv + h) * a.dv + c0 + cc;
         float acc[kItemCols];
 #pragma unroll
-        for (int c = 0; c < kItemCols; ++c) acc[c] = 0.f;
-#pragma unroll
-        for (int d = 0; d < DK; ++d) {
-            const float qd = unpack(qp, d);
-            const float4 *row = reinterpret_cast<const float4 *>(S0b + d * kColBlock + cc);
-#pragma unroll
-            for (int c4 = 0; c4 < kItemCols / 4; ++c4) {
-                const float4 s = row[c4];
-                acc[4 * c4 + 0] = fmaf(qd, s.x, acc[4 * c4 + 0]);
-                acc[4 * c4 + 1] = fmaf(qd, s.y, acc[4 * c4 + 1]);
-                acc[4 * c4 + 2] = fmaf(qd, s.z, acc[4 * c4 + 2]);
-                acc[4 * c4 + 3] = fmaf(qd, s.w, acc[4 * c4 + 3]);
-            }
+        for (int c4 = 0; c4 < kItemCols / 4; ++c4) {
+            const float4 w = reinterpret_cast<const float4 *>(orow)[c4];
+            acc[4 * c4] = w.x;
+            acc[4 * c4 + 1] = w.y;
+            acc[4 * c4 + 2] = w.z;
+            acc[4 * c4 + 3] = w.w;
         }
-        const float gt = G[t], eg = __expf(gt);
-#pragma unroll
-        for (int c = 0; c < kItemCols; ++c) acc[c] *= eg;
-        for (int j = t; j >= 0; j = tr.par[j]) {
-            const float y = __expf(gt - G[j]) * dot_reg_lds<DK>(qp, Ks + j * DK);
+        const float gt = G[t];
+        int m = 0;
+        for (int j = t; j >= 0; j = tr.par[j], ++m) {
+            float y;
+            if (m < kAncCap) {
+                y = YA[t * kAncCap + m];
+            } else {
+                uint32_t qp[DK / 2];
+                load_row<DK>(qp, qg + (((int64_t)b * T + t) * a.Hk + hk) * DK);
+                y = __expf(gt - G[j]) * dot_reg_lds<DK>(qp, Ks + j * KS);
+            }
 #pragma unroll
             for (int c = 0; c < kItemCols; ++c) acc[c] = fmaf(y, U[j * kColBlock + cc + c], acc[c]);
         }
-        float *orow = a.o + (((int64_t)b * T + t) * a.Hv + h) * a.dv + c0 + cc;
 #pragma unroll
         for (int c4 = 0; c4 < kItemCols / 4; ++c4)
             reinterpret_cast<float4 *>(orow)[c4] =
