@@ -255,7 +255,11 @@ int tree_spec_sample(const float *p, const float *q, int64_t row_stride, int B, 
                      const double *u_sample, void *ws, size_t ws_bytes, int32_t *accept_len,
                      int32_t *path, int32_t *next_token, int32_t *err_flag, hipStream_t stream);
 
-/* Host-only. Workspace bytes tree_spec_sample needs: B * (T + 1) * ceil(V / 4096) doubles. */
+/*
+ * Host-only. Workspace bytes tree_spec_sample needs: two arrays of B * (T + 1) * ceil(V / 4096)
+ * doubles (chunk sums of the residual masses) and B arrival counters of the workgroups that
+ * share a sequence's row passes.
+ */
 int tree_spec_sample_workspace_size(int B, int T, int V, size_t *bytes);
 
 /*

@@ -396,11 +396,18 @@ static int check_spec(int B, int T, int V) {
     return TA_OK;
 }
 
+// Workspace of tree_spec_sample: mass chunk sums, pass chunk sums (both B (T + 1) nch doubles),
+// then B arrival counters.
+static size_t spec_ws_bytes(int B, int T, int V) {
+    const size_t n = (size_t)B * (T + 1) * ta::spec_sample_chunks(V);
+    return align256(2 * n * sizeof(double) + (size_t)B * sizeof(uint32_t));
+}
+
 int tree_spec_sample_workspace_size(int B, int T, int V, size_t *bytes) {
     int rc = check_spec(B, T, V);
     if (rc) return rc;
     if (!bytes) return TA_EINVAL;
-    *bytes = align256((size_t)B * (T + 1) * ta::spec_sample_chunks(V) * sizeof(double));
+    *bytes = spec_ws_bytes(B, T, V);
     return TA_OK;
 }
 
@@ -416,11 +423,13 @@ int tree_spec_sample(const float *p, const float *q, int64_t row_stride, int B, 
         !next_token)
         return TA_EINVAL;
     if (!aligned16(p) || !aligned16(q)) return TA_EINVAL;
-    const size_t need = (size_t)B * (T + 1) * ta::spec_sample_chunks(V) * sizeof(double);
-    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) return TA_EWORKSPACE;
-    ta::SpecArgs a{p, q, row_stride, B, T, V, draft, parent, u_accept, u_sample,
-                   static_cast<double *>(ws), accept_len, path, next_token, err_flag};
-    return status(ta::launch_spec_sample(a, stream));
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < spec_ws_bytes(B, T, V)) return TA_EWORKSPACE;
+    const size_t n = (size_t)B * (T + 1) * ta::spec_sample_chunks(V);
+    double *sums = static_cast<double *>(ws);
+    ta::SpecArgs a{p, q, row_stride, B, T, V, draft, parent, u_accept, u_sample, sums, sums + n,
+                   reinterpret_cast<uint32_t *>(sums + 2 * n), accept_len, path, next_token,
+                   err_flag};
+    return status(ta::launch_spec_sample(a, cu_count(), stream));
 }
 
 static int check_gdn(int B, int T, int Hk, int Hv, int dk, int dv) {

@@ -108,13 +108,15 @@ struct SpecArgs {
     const int32_t *draft, *parent;
     const double *u_accept;  // [B, T]
     const double *u_sample;  // [B]
-    double *sums;            // workspace: [B * (T + 1)][spec_sample_chunks(V)] chunk sums
+    double *sums;            // workspace: [B * (T + 1)][nch] chunk sums of the mass kernel
+    double *pass_sums;       // workspace: [B][T + 1][nch] chunk sums of the walk's row passes
+    uint32_t *counters;      // workspace: [B] arrival counters of the walk's workgroups
     int32_t *accept_len, *path, *next_token, *err;
 };
 
 // 4096-entry chunks per row of tree speculative sampling.
 int spec_sample_chunks(int V);
-hipError_t launch_spec_sample(const SpecArgs &a, hipStream_t s);
+hipError_t launch_spec_sample(const SpecArgs &a, int cus, hipStream_t s);
 
 // Chunks per logits row for the argmax (the workspace holds B * (T + 1) * chunks int2 winners).
 int greedy_accept_chunks(int V, bool bf16);

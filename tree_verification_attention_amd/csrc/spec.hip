@@ -33,7 +33,8 @@ namespace ta {
 namespace {
 
 constexpr int kMassThreads = 256;
-constexpr int kWalkThreads = 1024;
+constexpr int kWalkThreads = 256;
+constexpr int kSpinLimit = 1 << 20;      // polls before a workgroup stops waiting for its peers
 constexpr int kChunk = 4096;              // entries per chunk (1024 float4)
 constexpr int kChunkVec = kChunk / 4;
 
@@ -69,8 +70,11 @@ __device__ inline bool position_has_child(const int32_t *parent, int T, int pos)
 __global__ __launch_bounds__(kMassThreads) void spec_mass_kernel(const float *p, const float *q,
                                                                  int64_t row_stride, int T, int V,
                                                                  int nch, const int32_t *parent,
-                                                                 double *sums) {
+                                                                 double *sums, uint32_t *counters,
+                                                                 int B) {
     const int chunk = blockIdx.x;
+    if (chunk == 0 && blockIdx.y == 0)  // the walk's arrival counters start at zero
+        for (int i = threadIdx.x; i < B; i += kMassThreads) counters[i] = 0u;
     const int row_id = blockIdx.y;  // b * (T + 1) + row
     const int b = row_id / (T + 1), row = row_id % (T + 1);
     const bool use_q = position_has_child(parent + (int64_t)b * T, T, row - 1);
@@ -110,53 +114,80 @@ struct WalkShared {
     float pv[TA_MAX_TREE];             // p(x) and q(x) of every node's draft token at its row
     float qv[TA_MAX_TREE];
     double n2[TA_MAX_TREE + 1];        // N_2 of every row with children
-    double cs[TA_MAX_VOCAB / kChunk];  // chunk sums of the residual of the last row pass
+    double cs[TA_MAX_VOCAB / kChunk];  // chunk sums of the current final weights
     double red[kWalkThreads / 64];
     int32_t path[TA_MAX_TREE];
-    // walk state (written by thread 0)
-    int32_t pos, child, k, n_path, have_pass, done, bonus, found;
+    // walk state (written by thread 0; every workgroup of a sequence holds the same)
+    int32_t pos, child, k, n_path, have_pass, done, bonus, n_pass, pass_ok;
     double Cprev, Nk, pass_C, pass_N, theta, base;
     int32_t pass_row, chunk_hit;
 };
 
-// Sum of R over chunk ch of one row, by one wavefront (result in every lane).
-__device__ inline double chunk_sum_wave(const float *pr, const float *qr, double C, bool use_q,
-                                        int ch, int nch, int V) {
-    const int lane = threadIdx.x & 63;
-    const int nvec = V / 4;
+// Sum of R = [p - C q]_+ (or p) over chunk ch of one row, by the whole workgroup; the result is
+// valid in thread 0. Fixed thread mapping and order, so every workgroup gets the same bits.
+__device__ inline double chunk_sum_block(const float *pr, const float *qr, double C, bool use_q,
+                                         int ch, int nch, int V, double *red) {
+    const int tid = threadIdx.x, nvec = V / 4;
     double s = 0.0;
-#pragma unroll 4
-    for (int k = 0; k < kChunkVec / 64; ++k) {
-        const int v = ch * kChunkVec + k * 64 + lane;
-        if (v < nvec)
-            s += entry4(reinterpret_cast<const float4 *>(pr)[v],
-                        use_q ? reinterpret_cast<const float4 *>(qr)[v] : make_float4(0, 0, 0, 0),
-                        C, use_q);
+    float4 pv[kChunkVec / kWalkThreads], qv[kChunkVec / kWalkThreads];
+#pragma unroll
+    for (int k = 0; k < kChunkVec / kWalkThreads; ++k) {
+        const int v = ch * kChunkVec + k * kWalkThreads + tid;
+        pv[k] = v < nvec ? reinterpret_cast<const float4 *>(pr)[v] : make_float4(0, 0, 0, 0);
+        qv[k] = use_q && v < nvec ? reinterpret_cast<const float4 *>(qr)[v]
+                                  : make_float4(0, 0, 0, 0);
     }
+#pragma unroll
+    for (int k = 0; k < kChunkVec / kWalkThreads; ++k) s += entry4(pv[k], qv[k], C, use_q);
     if (ch == nch - 1)
-        for (int e = nvec * 4 + lane; e < V; e += 64) s += entry(pr[e], use_q ? qr[e] : 0.f, C, use_q);
-    return wave_sum(s);
+        for (int e = nvec * 4 + tid; e < V; e += kWalkThreads) s += entry(pr[e], use_q ? qr[e] : 0.f, C, use_q);
+    s = wave_sum(s);
+    __syncthreads();  // red is free
+    if ((tid & 63) == 0) red[tid >> 6] = s;
+    __syncthreads();
+    double t = 0.0;
+    if (tid == 0)
+        for (int w = 0; w < kWalkThreads / 64; ++w) t += red[w];
+    return t;
 }
 
-__global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(
-    const float *p, const float *q, int64_t row_stride, int T, int V, int nch,
-    const int32_t *draft, const int32_t *parent, const double *u_accept, const double *u_sample,
-    const double *sums, int32_t *accept_len, int32_t *path, int32_t *next_token, int32_t *err) {
+// One sequence is walked by G workgroups (blockIdx.x = g). They hold identical walk state and
+// take identical decisions; a row pass is split between them (chunk c by workgroup c mod G),
+// its chunk sums meet in the workspace, and a counter per sequence tells when all have arrived.
+// A workgroup that waits too long (its peers not resident) computes the missing chunks itself
+// with the same arithmetic, so the decisions never depend on the schedule.
+__global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int nch, int G) {
     __shared__ WalkShared sh;
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float *p = a.p, *q = a.q;
+    const int64_t row_stride = a.row_stride;
+    const int T = a.T, V = a.V;
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t row0 = (int64_t)b * (T + 1);
+    int32_t *err = a.err;
     for (int r = tid; r <= T; r += kWalkThreads) sh.first_child[r] = INT32_MAX;
+    int pa = -1, x = 0;
     if (tid < T) {
-        int pa = parent[(int64_t)b * T + tid];
+        pa = a.parent[(int64_t)b * T + tid];
+        x = a.draft[(int64_t)b * T + tid];
         if (pa < -1 || pa >= tid) {
-            if (err) atomicOr(err, (int32_t)TA_DEV_BAD_PARENT);
+            if (err && g == 0) atomicOr(err, (int32_t)TA_DEV_BAD_PARENT);
             pa = -1;
         }
         sh.par[tid] = pa;
+        // p(x) and q(x) of the node's draft token, at its parent's row
+        const int64_t ro = (row0 + pa + 1) * row_stride;
+        if (x >= 0 && x < V) {
+            sh.pv[tid] = p[ro + x];
+            sh.qv[tid] = q[ro + x];
+        } else {
+            // a token outside the vocabulary has no target mass: it is always rejected
+            if (err && g == 0) atomicOr(err, (int32_t)TA_DEV_BAD_TOKEN);
+            sh.pv[tid] = 0.f;
+            sh.qv[tid] = 1.f;
+        }
     }
     __syncthreads();
     if (tid < T) {
-        const int pa = sh.par[tid];
         atomicMin(&sh.first_child[pa + 1], tid);
         int nx = -1;
         for (int j = tid + 1; j < T; ++j)
@@ -165,29 +196,22 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(
                 break;
             }
         sh.next_sib[tid] = nx;
-        // p(x) and q(x) of the node's draft token, at its parent's row
-        const int x = draft[(int64_t)b * T + tid];
-        const int64_t ro = (row0 + pa + 1) * row_stride;
-        if (x >= 0 && x < V) {
-            sh.pv[tid] = p[ro + x];
-            sh.qv[tid] = q[ro + x];
-        } else {
-            // a token outside the vocabulary has no target mass: it is always rejected
-            if (err) atomicOr(err, (int32_t)TA_DEV_BAD_TOKEN);
-            sh.pv[tid] = 0.f;
-            sh.qv[tid] = 1.f;
-        }
     }
     __syncthreads();
-    if (tid <= T) {
-        const bool has_child = sh.first_child[tid] != INT32_MAX;
-        if (!has_child) sh.first_child[tid] = -1;
-        double n = 0.0;  // N_2 of the row, summed over its chunks in order
+    // N_2 of every row with children, one wavefront per row: lane l sums chunks l, l + 64, ...,
+    // then a butterfly (T + 1 rows: one more than nodes)
+    for (int r = wave; r <= T; r += kWalkThreads / 64) {
+        const bool has_child = sh.first_child[r] != INT32_MAX;
+        double n = 0.0;
         if (has_child) {
-            const double *sr = sums + (row0 + tid) * nch;
-            for (int c = 0; c < nch; ++c) n += sr[c];
+            const double *sr = a.sums + (row0 + r) * nch;
+            for (int c = lane; c < nch; c += 64) n += sr[c];
+            n = wave_sum(n);
         }
-        sh.n2[tid] = n;
+        if (lane == 0) {
+            sh.n2[r] = n;
+            if (!has_child) sh.first_child[r] = -1;
+        }
     }
     if (tid == 0) {
         sh.pos = -1;
@@ -195,9 +219,10 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(
         sh.n_path = 0;
         sh.have_pass = 0;
         sh.done = 0;
+        sh.n_pass = 0;
     }
     __syncthreads();
-    // -------- the walk: thread 0 advances it; the block makes the row passes it asks for -------
+    // -------- the walk: thread 0 advances it; the workgroups make the row passes it asks for --
     for (;;) {
         if (tid == 0) {
             for (;;) {
@@ -220,14 +245,14 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(
                     n_next = sh.n2[row];
                 } else if (sh.have_pass) {
                     n_next = sh.pass_N;
-                } else {  // N_{k+1} = sum [p - C_k q]_+ : ask the block for a pass over the row
+                } else {  // N_{k+1} = sum [p - C_k q]_+ : ask for a pass over the row
                     sh.pass_row = row;
                     sh.pass_C = sh.Cprev + sh.Nk;
                     break;
                 }
                 const double R = fmax(0.0, (double)sh.pv[c] - sh.Cprev * (double)sh.qv[c]);
                 const bool accept =
-                    n_next == 0.0 || u_accept[(int64_t)b * T + c] * sh.Nk * (double)sh.qv[c] < R;
+                    n_next == 0.0 || a.u_accept[(int64_t)b * T + c] * sh.Nk * (double)sh.qv[c] < R;
                 if (accept) {
                     sh.path[sh.n_path++] = c;
                     sh.pos = c;
@@ -248,23 +273,62 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(
         }
         __syncthreads();
         if (sh.done) break;
-        // row pass: chunk sums of [p - pass_C q]_+ into cs, their total into pass_N
-        {
-            const int64_t ro = (row0 + sh.pass_row) * row_stride;
-            const double C = sh.pass_C;
-            for (int ch = wave; ch < nch; ch += kWalkThreads / 64) {
-                const double s = chunk_sum_wave(p + ro, q + ro, C, true, ch, nch, V);
-                if (lane == 0) sh.cs[ch] = s;
-            }
-            __syncthreads();
+        // row pass: this workgroup's chunks of [p - pass_C q]_+, then everyone's
+        const int64_t ro = (row0 + sh.pass_row) * row_stride;
+        const double C = sh.pass_C;
+        const int pass = sh.n_pass;
+        double *buf = a.pass_sums + ((int64_t)b * (T + 1) + pass) * nch;
+        for (int ch = g; ch < nch; ch += G) {
+            const double s = chunk_sum_block(p + ro, q + ro, C, true, ch, nch, V, sh.red);
             if (tid == 0) {
-                double n = 0.0;
-                for (int c = 0; c < nch; ++c) n += sh.cs[c];
+                buf[ch] = s;
+                sh.cs[ch] = s;
+            }
+        }
+        if (tid == 0) {
+            int ok = 1;
+            if (G > 1) {
+                __threadfence();
+                atomicAdd(a.counters + b, 1u);
+                const unsigned target = (unsigned)(pass + 1) * (unsigned)G;
+                for (int spin = 0;; ++spin) {
+                    if (__hip_atomic_load(a.counters + b, __ATOMIC_ACQUIRE,
+                                          __HIP_MEMORY_SCOPE_AGENT) >= target)
+                        break;
+                    if (spin >= kSpinLimit) {
+                        ok = 0;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            sh.pass_ok = ok;
+        }
+        __syncthreads();
+        if (sh.pass_ok) {
+            for (int ch = tid; ch < nch; ch += kWalkThreads)
+                if (ch % G != g)
+                    sh.cs[ch] = __hip_atomic_load(buf + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            for (int ch = 0; ch < nch; ++ch)
+                if (ch % G != g) {
+                    const double s = chunk_sum_block(p + ro, q + ro, C, true, ch, nch, V, sh.red);
+                    if (tid == 0) sh.cs[ch] = s;
+                }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // N_{k+1}: lane l sums chunks l, l + 64, ..., then a butterfly (a fixed order)
+            double n = 0.0;
+            for (int c = lane; c < nch; c += 64) n += sh.cs[c];
+            n = wave_sum(n);
+            if (lane == 0) {
                 sh.pass_N = n;
                 sh.have_pass = 1;
+                sh.n_pass = pass + 1;
             }
-            __syncthreads();
         }
+        __syncthreads();
     }
     // -------- the emitted token --------
     const int row = sh.pos + 1;
@@ -272,39 +336,70 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(
     const bool use_q = !sh.bonus;
     const double C = sh.Cprev;
     // chunk sums of the final weights: the mass kernel's (bonus: p; correction after one trial:
-    // [p - q]_+), else the last row pass's
+    // [p - q]_+), else those of the last row pass (already in cs)
     const bool from_pass = !sh.bonus && sh.k > 2;
     if (!from_pass)
-        for (int c = tid; c < nch; c += kWalkThreads) sh.cs[c] = sums[(row0 + row) * nch + c];
+        for (int c = tid; c < nch; c += kWalkThreads) sh.cs[c] = a.sums[(row0 + row) * nch + c];
     __syncthreads();
-    if (tid == 0) {
-        double w = 0.0;
-        for (int c = 0; c < nch; ++c) w += sh.cs[c];
-        sh.theta = u_sample[b] * w;
-        // the first chunk whose running sum passes theta
-        double cum = 0.0;
+    if (wave == 0) {
+        // running sums of the chunk sums: lane l holds chunks 4l .. 4l + 3 (nch <= 256)
+        double cl[4], own = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 4 * lane + i;
+            cl[i] = c < nch ? sh.cs[c] : 0.0;
+            own += cl[i];
+        }
+        double incl = own;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const double o = __shfl_up(incl, m);
+            if (lane >= m) incl += o;
+        }
+        const double total = __shfl(incl, 63);
+        const double theta = a.u_sample[b] * total;
+        // the first chunk whose running sum passes theta, and the last chunk with mass
+        double cum = incl - own;
         int hit = -1, last_pos = -1;
-        for (int c = 0; c < nch; ++c) {
-            if (sh.cs[c] > 0.0) last_pos = c;
-            if (hit < 0 && cum + sh.cs[c] > sh.theta) {
-                hit = c;
-                sh.base = cum;
+        double base = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (cl[i] > 0.0) last_pos = 4 * lane + i;
+            if (hit < 0 && cum + cl[i] > theta) {
+                hit = 4 * lane + i;
+                base = cum;
             }
-            cum += sh.cs[c];
+            cum += cl[i];
         }
-        if (hit < 0) {  // rounding left theta past the total: the last chunk with mass
-            hit = last_pos < 0 ? 0 : last_pos;
-            sh.base = -INFINITY;  // no entry passes: take the chunk's last positive entry
+        const uint64_t hits = __ballot(hit >= 0);
+        int lp = last_pos;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) lp = max(lp, __shfl_xor(lp, m));
+        const int first = hits ? __builtin_ctzll(hits) : -1;
+        if (lane == (first < 0 ? 0 : first)) {
+            sh.theta = theta;
+            if (first >= 0) {
+                sh.chunk_hit = hit;
+                sh.base = base;
+            } else {  // rounding left theta past the total: the last chunk with mass
+                sh.chunk_hit = lp < 0 ? 0 : lp;
+                sh.base = -INFINITY;  // no entry passes: take the chunk's last positive entry
+            }
+            if (g == 0) a.accept_len[b] = sh.n_path;
         }
-        sh.chunk_hit = hit;
-        sh.found = INT32_MAX;
     }
     __syncthreads();
+    if (g == 0)
+        for (int j = tid; j < T; j += kWalkThreads)
+            a.path[(int64_t)b * T + j] = j < sh.n_path ? sh.path[j] : -1;
+    if (sh.chunk_hit % G != g) return;  // the chunk's owner draws the token
     {
-        const int e0 = sh.chunk_hit * kChunk + 4 * tid;  // this thread's 4 entries
-        double w[4], t = 0.0;
+        // this thread's entries e0 .. e0 + kEntries - 1 of the chunk
+        constexpr int kEntries = kChunk / kWalkThreads;
+        const int e0 = sh.chunk_hit * kChunk + kEntries * tid;
+        double w[kEntries], t = 0.0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kEntries; ++j) {
             const int e = e0 + j;
             w[j] = e < V ? entry(p[ro + e], use_q ? q[ro + e] : 0.f, C, use_q) : 0.0;
             t += w[j];
@@ -323,7 +418,7 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(
         double run = sh.base + before + incl - t;
         int hit = INT32_MAX, lastp = -1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kEntries; ++j) {
             run += w[j];
             if (hit == INT32_MAX && run > sh.theta) hit = e0 + j;
             if (w[j] > 0.0) lastp = e0 + j;
@@ -335,7 +430,6 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(
         int lkey = lastp;
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) lkey = max(lkey, __shfl_xor(lkey, m));
-        __syncthreads();
         __shared__ int s_min[kWalkThreads / 64], s_last[kWalkThreads / 64];
         if (lane == 0) {
             s_min[wave] = key;
@@ -348,26 +442,25 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(
                 k2 = min(k2, s_min[w2]);
                 l2 = max(l2, s_last[w2]);
             }
-            next_token[b] = k2 != INT32_MAX ? k2 : (l2 >= 0 ? l2 : 0);
-            accept_len[b] = sh.n_path;
+            a.next_token[b] = k2 != INT32_MAX ? k2 : (l2 >= 0 ? l2 : 0);
         }
     }
-    for (int j = tid; j < T; j += kWalkThreads) path[(int64_t)b * T + j] = j < sh.n_path ? sh.path[j] : -1;
 }
 
 }  // namespace
 
 int spec_sample_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
-hipError_t launch_spec_sample(const SpecArgs &a, hipStream_t s) {
+hipError_t launch_spec_sample(const SpecArgs &a, int cus, hipStream_t s) {
     const int nch = spec_sample_chunks(a.V);
+    // workgroups per sequence: one per chunk, as far as the compute units go
+    int G = cus / (a.B > 0 ? a.B : 1);
+    G = G < 1 ? 1 : (G > nch ? nch : G);
     hipLaunchKernelGGL(spec_mass_kernel, dim3(nch, a.B * (a.T + 1)), dim3(kMassThreads), 0, s, a.p,
-                       a.q, a.row_stride, a.T, a.V, nch, a.parent, a.sums);
+                       a.q, a.row_stride, a.T, a.V, nch, a.parent, a.sums, a.counters, a.B);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(spec_walk_kernel, dim3(a.B), dim3(kWalkThreads), 0, s, a.p, a.q,
-                       a.row_stride, a.T, a.V, nch, a.draft, a.parent, a.u_accept, a.u_sample,
-                       a.sums, a.accept_len, a.path, a.next_token, a.err);
+    hipLaunchKernelGGL(spec_walk_kernel, dim3(G, a.B), dim3(kWalkThreads), 0, s, a, nch, G);
     return hipGetLastError();
 }
 
