@@ -447,7 +447,7 @@ def accept_stats_summary(stats_dir, steps):
         m = re.search(r'^\{.*\}$', open(logs[0]).read(), re.M)
         bench = json.loads(m.group(0)) if m else None
     os.makedirs(PROFILES, exist_ok=True)
-    out = os.path.join(PROFILES, "argmax_kernel_greedy_accept_b4_t64_v128256_stats.txt")
+    out = os.path.join(PROFILES, "next_rows_accept_sampling_gdn_commit_stats.txt")
     lines = [
         "# rocprofv3 kernel statistics, greedy tree acceptance (B=4, T=64, vocab 128256, bf16 "
         "logits), tree speculative sampling (same tree and vocabulary, fp32 p and q) and "
