@@ -450,8 +450,9 @@ def accept_stats_summary(stats_dir, steps):
     out = os.path.join(PROFILES, "next_rows_accept_sampling_gdn_commit_stats.txt")
     lines = [
         "# rocprofv3 kernel statistics, greedy tree acceptance (B=4, T=64, vocab 128256, bf16 "
-        "logits), tree speculative sampling (same tree and vocabulary, fp32 p and q) and "
-        "accepted-path KV commit (B=4, Hkv=8, D=128 bf16)",
+        "logits), tree speculative sampling (same tree and vocabulary, fp32 p and q), GDN tree "
+        "verification (B=4, T=128, H_k=16, H_v=32, d_k=d_v=128) and accepted-path KV commit "
+        "(B=4, Hkv=8, D=128 bf16)",
         f"# command: rocprofv3 --kernel-trace --stats -d STATS_DIR -o run --output-format csv -- "
         f"python3 bench.py --next-rows-only --steps {steps} --warmup 5",
         f"# summary: python3 bench.py --steps {steps} --accept-stats-summary STATS_DIR",
