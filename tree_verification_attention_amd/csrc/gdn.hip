@@ -289,19 +289,42 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
             float u[kItemCols];
 #pragma unroll
             for (int c = 0; c < kItemCols; ++c) u[c] = U[t * kColBlock + cc + c];
-            const float bt = tr.beta[t], gt = G[t];
-            int m = 1;
-            for (int j = tr.par[t]; j >= 0; j = tr.par[j], ++m) {
-                float x;
-                if (m < kAncCap) {
-                    x = XA[t * kAncCap + m];
-                } else {  // deep paths: the coefficient on the spot
-                    uint32_t kp[DK / 2];
-                    load_row<DK>(kp, Ks + t * KS);
-                    x = bt * __expf(gt - G[j]) * dot_reg_lds<DK>(kp, Ks + j * KS);
+            // ancestors at path positions 1 .. nd from the tables, four at a time so that their
+            // loads overlap; deeper ones (past the tables) one by one with the coefficient on the
+            // spot
+            const int nd = min(dep[t] - 1, kAncCap - 1);
+            for (int m0 = 1; m0 <= nd; m0 += 4) {
+                float x[4];
+                float4 uj[4][kItemCols / 4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = m0 + i <= nd;
+                    const int j = ok ? anc[t * kAncCap + m0 + i] : t;
+                    x[i] = ok ? XA[t * kAncCap + m0 + i] : 0.f;
+#pragma unroll
+                    for (int c4 = 0; c4 < kItemCols / 4; ++c4)
+                        uj[i][c4] = *reinterpret_cast<const float4 *>(U + j * kColBlock + cc + 4 * c4);
                 }
 #pragma unroll
-                for (int c = 0; c < kItemCols; ++c) u[c] = fmaf(-x, U[j * kColBlock + cc + c], u[c]);
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int c4 = 0; c4 < kItemCols / 4; ++c4) {
+                        u[4 * c4 + 0] = fmaf(-x[i], uj[i][c4].x, u[4 * c4 + 0]);
+                        u[4 * c4 + 1] = fmaf(-x[i], uj[i][c4].y, u[4 * c4 + 1]);
+                        u[4 * c4 + 2] = fmaf(-x[i], uj[i][c4].z, u[4 * c4 + 2]);
+                        u[4 * c4 + 3] = fmaf(-x[i], uj[i][c4].w, u[4 * c4 + 3]);
+                    }
+            }
+            if (dep[t] > kAncCap) {
+                const float bt = tr.beta[t], gt = G[t];
+                uint32_t kp[DK / 2];
+                load_row<DK>(kp, Ks + t * KS);
+                for (int j = tr.par[anc[t * kAncCap + kAncCap - 1]]; j >= 0; j = tr.par[j]) {
+                    const float x = bt * __expf(gt - G[j]) * dot_reg_lds<DK>(kp, Ks + j * KS);
+#pragma unroll
+                    for (int c = 0; c < kItemCols; ++c)
+                        u[c] = fmaf(-x, U[j * kColBlock + cc + c], u[c]);
+                }
             }
 #pragma unroll
             for (int c = 0; c < kItemCols; ++c) U[t * kColBlock + cc + c] = u[c];
@@ -321,19 +344,39 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
             acc[4 * c4 + 2] = w.z;
             acc[4 * c4 + 3] = w.w;
         }
-        const float gt = G[t];
-        int m = 0;
-        for (int j = t; j >= 0; j = tr.par[j], ++m) {
-            float y;
-            if (m < kAncCap) {
-                y = YA[t * kAncCap + m];
-            } else {
-                uint32_t qp[DK / 2];
-                load_row<DK>(qp, qg + (((int64_t)b * T + t) * a.Hk + hk) * DK);
-                y = __expf(gt - G[j]) * dot_reg_lds<DK>(qp, Ks + j * KS);
+        // path positions 0 .. nd from the tables, four at a time; deeper ones one by one
+        const int nd = min(dep[t] - 1, kAncCap - 1);
+        for (int m0 = 0; m0 <= nd; m0 += 4) {
+            float y[4];
+            float4 uj[4][kItemCols / 4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = m0 + i <= nd;
+                const int j = ok ? anc[t * kAncCap + m0 + i] : t;
+                y[i] = ok ? YA[t * kAncCap + m0 + i] : 0.f;
+#pragma unroll
+                for (int c4 = 0; c4 < kItemCols / 4; ++c4)
+                    uj[i][c4] = *reinterpret_cast<const float4 *>(U + j * kColBlock + cc + 4 * c4);
             }
 #pragma unroll
-            for (int c = 0; c < kItemCols; ++c) acc[c] = fmaf(y, U[j * kColBlock + cc + c], acc[c]);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c4 = 0; c4 < kItemCols / 4; ++c4) {
+                    acc[4 * c4 + 0] = fmaf(y[i], uj[i][c4].x, acc[4 * c4 + 0]);
+                    acc[4 * c4 + 1] = fmaf(y[i], uj[i][c4].y, acc[4 * c4 + 1]);
+                    acc[4 * c4 + 2] = fmaf(y[i], uj[i][c4].z, acc[4 * c4 + 2]);
+                    acc[4 * c4 + 3] = fmaf(y[i], uj[i][c4].w, acc[4 * c4 + 3]);
+                }
+        }
+        if (dep[t] > kAncCap) {
+            const float gt = G[t];
+            uint32_t qp[DK / 2];
+            load_row<DK>(qp, qg + (((int64_t)b * T + t) * a.Hk + hk) * DK);
+            for (int j = tr.par[anc[t * kAncCap + kAncCap - 1]]; j >= 0; j = tr.par[j]) {
+                const float y = __expf(gt - G[j]) * dot_reg_lds<DK>(qp, Ks + j * KS);
+#pragma unroll
+                for (int c = 0; c < kItemCols; ++c) acc[c] = fmaf(y, U[j * kColBlock + cc + c], acc[c]);
+            }
         }
 #pragma unroll
         for (int c4 = 0; c4 < kItemCols / 4; ++c4)
