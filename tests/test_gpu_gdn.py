@@ -42,6 +42,7 @@ CASES = [
     ("star", dict(B=2, T=50, Hk=2, Hv=2, dk=128, dv=32), {"tree": "star"}),
     ("uniform", dict(B=2, T=100, Hk=1, Hv=3, dk=64, dv=128), {"tree": "uniform"}),
     ("one_node", dict(B=3, T=1, Hk=2, Hv=4, dk=128, dv=32), {"tree": "single"}),
+    ("dk64_dv256_t200", dict(B=1, T=200, Hk=1, Hv=2, dk=64, dv=256), {"depth_cap": 24}),
 ]
 
 

@@ -71,6 +71,14 @@ def test_spec_sample(name, shape, kw):
         assert n.max() == 0
 
 
+def test_spec_sample_largest_vocabulary():
+    # 2^20 entries per row: 256 chunks, every lane of the chunk search holding four
+    case = inputs.make_spec_case(2, 3, 1 << 20, 8, tree="chain", noise=2.0)
+    check(case, "vocab 2^20")
+    case.u_accept[:] = 0.999                 # rejections: corrections drawn over 256 chunks
+    check(case, "vocab 2^20, corrections")
+
+
 def test_spec_sample_many_seeds_and_ragged_rows():
     for seed in range(8):
         case = inputs.make_spec_case(6, 32, 4099, seed, noise=1.5)
