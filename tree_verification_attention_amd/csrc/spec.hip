@@ -17,10 +17,11 @@
 // spec_mass_kernel (data-parallel, HBM-bound): per (row, 4096-entry chunk), the chunk's sum of
 //   [p - q]_+ when the row's position has children (N_2's parts: a first rejection there needs
 //   it), else of p (the bonus token's weights).
-// spec_walk_kernel: one workgroup per sequence. The per-node values p(x), q(x) are gathered up
-//   front, so the walk itself reads LDS only; a second trial at one position needs N_{k+1} for
-//   k >= 2, which the workgroup computes with a pass over that row; the final token is located
-//   chunk by chunk from the chunk sums, then inside its chunk by a block prefix sum.
+// spec_walk_kernel: G workgroups per sequence, all walking the same tree with the same state.
+//   The per-node values p(x), q(x) are gathered up front, so the walk itself reads LDS only; a
+//   second trial at one position needs N_{k+1} for k >= 2, a pass over that row which the G
+//   workgroups split by chunks and meet on through the workspace; the final token's chunk is
+//   found from the chunk sums, then its owner scans it with a block prefix sum.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
