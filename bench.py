@@ -366,6 +366,40 @@ def copy_calibration(n=5):
     torch.cuda.synchronize()
 
 
+UTIL_COUNTERS = ("MfmaUtil", "LdsBankConflict", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+                 "SQ_WAVES")
+
+
+def parse_util(util_dir, workload):
+    """Per-dispatch averages of the utilisation counters of the dominant kernel (one rocprofv3
+    --pmc pass of UTIL_COUNTERS) into a text summary under profiles/."""
+    vals = {}
+    for path in glob.glob(os.path.join(util_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if KERNEL_NAME in row["Kernel_Name"]:
+                    vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {KERNEL_NAME} dispatches under {util_dir}")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"{KERNEL_NAME}_{workload}_util.txt")
+    lines = [
+        f"# rocprofv3 utilisation counters of {KERNEL_NAME}, workload {workload}, mean per dispatch",
+        f"# command: rocprofv3 --pmc {' '.join(UTIL_COUNTERS)} -d UTIL_DIR -o run "
+        f"--output-format csv -- python3 bench.py --workload {workload} --steps 4 --warmup 1 "
+        f"--no-secondary --no-cpu-baseline --no-next-rows",
+        f"# summary: python3 bench.py --workload {workload} --parse-util UTIL_DIR",
+        "",
+    ]
+    for k in sorted(vals):
+        lines.append(f"{k}: {statistics.mean(vals[k]):.6g} ({len(vals[k])} dispatches)")
+    lines += ["", "MfmaUtil: percent of the cycles the MFMA units were busy; LdsBankConflict: percent of",
+              "LDS active cycles lost to bank conflicts (rocprofv3 derived metrics)."]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def parse_pmc(fetch_dir, write_dir, workload):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the attention and copy kernels, scaled by
     what the counters read for a plain copy of known size."""
@@ -547,6 +581,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB copies (reference for HBM counters)")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--parse-util", metavar="UTIL_DIR",
+                    help="summarise a rocprofv3 --pmc pass of the utilisation counters")
     ap.add_argument("--next-rows-only", action="store_true",
                     help="time only greedy acceptance and the KV commit; print their JSON")
     ap.add_argument("--accept-stats-summary", metavar="STATS_DIR",
@@ -561,6 +597,9 @@ def main():
 
     if args.accept_stats_summary:
         accept_stats_summary(args.accept_stats_summary, args.steps)
+        return
+    if args.parse_util:
+        parse_util(args.parse_util, args.workload)
         return
     if args.parse_pmc:
         parse_pmc(args.parse_pmc[0], args.parse_pmc[1], args.workload)
