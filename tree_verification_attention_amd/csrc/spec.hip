@@ -14,9 +14,8 @@
 // N_{k+1} == 0 (no rejection possible) or u * N_k * q(x) < R_k(x), which is u < min(1, r_k/q) for
 // q(x) > 0. Every sum runs in fp64 over the fp32 inputs.
 //
-// spec_mass_kernel (data-parallel, HBM-bound): per (row, 4096-entry chunk), the chunk's sum of
-//   [p - q]_+ when the row's position has children (N_2's parts: a first rejection there needs
-//   it), else of p (the bonus token's weights).
+// spec_mass_kernel (data-parallel, HBM-bound): per (row, 4096-entry chunk) of every position
+//   with children, the chunk's sum of [p - q]_+ (N_2's parts: a first rejection there needs it).
 // spec_walk_kernel: G workgroups per sequence, all walking the same tree with the same state.
 //   The per-node values p(x), q(x) are gathered up front, so the walk itself reads LDS only; a
 //   second trial at one position needs N_{k+1} for k >= 2, a pass over that row which the G
@@ -78,7 +77,10 @@ __global__ __launch_bounds__(kMassThreads) void spec_mass_kernel(const float *p,
         for (int i = threadIdx.x; i < B; i += kMassThreads) counters[i] = 0u;
     const int row_id = blockIdx.y;  // b * (T + 1) + row
     const int b = row_id / (T + 1), row = row_id % (T + 1);
-    const bool use_q = position_has_child(parent + (int64_t)b * T, T, row - 1);
+    // rows of positions without children are never needed here: a bonus token's weights come
+    // from a pass of the walk over the one row it ends on
+    if (!position_has_child(parent + (int64_t)b * T, T, row - 1)) return;
+    constexpr bool use_q = true;
     const float *pr = p + (int64_t)row_id * row_stride;
     const float *qr = q + (int64_t)row_id * row_stride;
     const int nvec = V / 4;
@@ -119,7 +121,7 @@ struct WalkShared {
     double red[kWalkThreads / 64];
     int32_t path[TA_MAX_TREE];
     // walk state (written by thread 0; every workgroup of a sequence holds the same)
-    int32_t pos, child, k, n_path, have_pass, done, bonus, n_pass, pass_ok;
+    int32_t pos, child, k, n_path, have_pass, done, bonus, n_pass, pass_ok, pass_q;
     double Cprev, Nk, pass_C, pass_N, theta, base;
     int32_t pass_row, chunk_hit;
 };
@@ -236,7 +238,14 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int
                     sh.have_pass = 0;
                 }
                 const int c = sh.child;
-                if (c < 0) {  // no children: bonus token from this row's p
+                if (c < 0) {  // no children: bonus token from this row's p, whose chunk sums a
+                              // pass over the row provides
+                    if (!sh.have_pass) {
+                        sh.pass_row = row;
+                        sh.pass_C = 0.0;
+                        sh.pass_q = 0;
+                        break;
+                    }
                     sh.bonus = 1;
                     sh.done = 1;
                     break;
@@ -249,6 +258,7 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int
                 } else {  // N_{k+1} = sum [p - C_k q]_+ : ask for a pass over the row
                     sh.pass_row = row;
                     sh.pass_C = sh.Cprev + sh.Nk;
+                    sh.pass_q = 1;
                     break;
                 }
                 const double R = fmax(0.0, (double)sh.pv[c] - sh.Cprev * (double)sh.qv[c]);
@@ -277,10 +287,11 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int
         // row pass: this workgroup's chunks of [p - pass_C q]_+, then everyone's
         const int64_t ro = (row0 + sh.pass_row) * row_stride;
         const double C = sh.pass_C;
+        const bool pq = sh.pass_q;
         const int pass = sh.n_pass;
         double *buf = a.pass_sums + ((int64_t)b * (T + 1) + pass) * nch;
         for (int ch = g; ch < nch; ch += G) {
-            const double s = chunk_sum_block(p + ro, q + ro, C, true, ch, nch, V, sh.red);
+            const double s = chunk_sum_block(p + ro, q + ro, C, pq, ch, nch, V, sh.red);
             if (tid == 0) {
                 buf[ch] = s;
                 sh.cs[ch] = s;
@@ -313,7 +324,7 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int
         } else {
             for (int ch = 0; ch < nch; ++ch)
                 if (ch % G != g) {
-                    const double s = chunk_sum_block(p + ro, q + ro, C, true, ch, nch, V, sh.red);
+                    const double s = chunk_sum_block(p + ro, q + ro, C, pq, ch, nch, V, sh.red);
                     if (tid == 0) sh.cs[ch] = s;
                 }
         }
@@ -336,9 +347,9 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int
     const int64_t ro = (row0 + row) * row_stride;
     const bool use_q = !sh.bonus;
     const double C = sh.Cprev;
-    // chunk sums of the final weights: the mass kernel's (bonus: p; correction after one trial:
-    // [p - q]_+), else those of the last row pass (already in cs)
-    const bool from_pass = !sh.bonus && sh.k > 2;
+    // chunk sums of the final weights: the mass kernel's for a correction after one trial
+    // ([p - q]_+), else those of the last row pass (already in cs; the bonus's pass sums p)
+    const bool from_pass = sh.bonus || sh.k > 2;
     if (!from_pass)
         for (int c = tid; c < nch; c += kWalkThreads) sh.cs[c] = a.sums[(row0 + row) * nch + c];
     __syncthreads();
