@@ -133,3 +133,59 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(TypeError):
         _lib.forward(q, q, q, torch.zeros(1, dtype=torch.int32), q[:, :, :1], q[:, :, :1],
                      torch.zeros(1, 2, dtype=torch.int32))
+
+
+FAKE = 1 << 20   # aligned non-null placeholder, never dereferenced: every call below is rejected
+
+
+def test_greedy_accept_rejects_bad_arguments_on_the_host(lib):
+    S = ctypes.c_size_t
+    n = S(0)
+    assert lib.tree_greedy_accept_workspace_size(_lib.TA_BF16, 4, 64, 128256, ctypes.byref(n)) == 0
+    assert n.value >= 4 * 65 * 8 and n.value % 256 == 0
+    assert lib.tree_greedy_accept_workspace_size(7, 4, 64, 100, ctypes.byref(n)) == _lib.TA_EUNSUPPORTED
+    assert lib.tree_greedy_accept_workspace_size(_lib.TA_BF16, 4, 257, 100, ctypes.byref(n)) == _lib.TA_EINVAL
+    args = lambda **kw: [kw.get("logits", FAKE), kw.get("dtype", _lib.TA_BF16),
+                         kw.get("stride", 128), 2, kw.get("T", 8), kw.get("V", 128), FAKE, FAKE,
+                         FAKE, kw.get("ws_bytes", 1 << 20), FAKE, FAKE, FAKE, FAKE, None, None]
+    assert lib.tree_greedy_accept(*args(stride=100)) == _lib.TA_EINVAL       # stride < V
+    assert lib.tree_greedy_accept(*args(V=124, stride=124)) == _lib.TA_EINVAL  # rows not 16-B apart
+    assert lib.tree_greedy_accept(*args(logits=FAKE + 2)) == _lib.TA_EINVAL   # misaligned base
+    assert lib.tree_greedy_accept(*args(ws_bytes=8)) == _lib.TA_EWORKSPACE
+    assert lib.tree_greedy_accept(*args(T=0)) == _lib.TA_EINVAL
+
+
+def test_spec_sample_rejects_bad_arguments_on_the_host(lib):
+    S = ctypes.c_size_t
+    n = S(0)
+    assert lib.tree_spec_sample_workspace_size(4, 64, 128256, ctypes.byref(n)) == 0
+    assert n.value >= 2 * 4 * 65 * 32 * 8
+    assert lib.tree_spec_sample_workspace_size(1, 8, (1 << 20) + 1, ctypes.byref(n)) == _lib.TA_EINVAL
+    args = lambda **kw: [kw.get("p", FAKE), FAKE, kw.get("stride", 1024), 2, 8,
+                         kw.get("V", 1024), FAKE, FAKE, FAKE, FAKE, FAKE,
+                         kw.get("ws_bytes", 1 << 20), FAKE, FAKE, FAKE, None, None]
+    assert lib.tree_spec_sample(*args(stride=1000)) == _lib.TA_EINVAL      # stride < V
+    assert lib.tree_spec_sample(*args(stride=1026, V=1025)) == _lib.TA_EINVAL  # rows misaligned
+    assert lib.tree_spec_sample(*args(p=FAKE + 4)) == _lib.TA_EINVAL
+    assert lib.tree_spec_sample(*args(ws_bytes=64)) == _lib.TA_EWORKSPACE
+
+
+def test_gdn_calls_reject_bad_arguments_on_the_host(lib):
+    f = ctypes.c_float(0.088)
+    base = dict(B=2, T=16, Hk=2, Hv=4, dk=128, dv=64)
+
+    def verify(**kw):
+        a = dict(base, **kw)
+        return lib.tree_gdn_verify(kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"],
+                                   a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"], f, FAKE, None, None)
+
+    assert verify(dk=96) == _lib.TA_EUNSUPPORTED
+    assert verify(dv=48) == _lib.TA_EUNSUPPORTED
+    assert verify(dv=288) == _lib.TA_EUNSUPPORTED
+    assert verify(Hv=6, Hk=4) == _lib.TA_EINVAL
+    assert verify(T=257) == _lib.TA_EINVAL
+    assert verify(q=FAKE + 2) == _lib.TA_EINVAL
+    assert verify(q=0) == _lib.TA_EINVAL
+    assert verify(B=0) == _lib.TA_OK
+    assert lib.tree_gdn_commit(FAKE, FAKE, FAKE, FAKE, 2, 16, 2, 4, 64, 64, FAKE, FAKE, 0,
+                               None, None) == _lib.TA_EINVAL
