@@ -257,8 +257,8 @@ int tree_spec_sample(const float *p, const float *q, int64_t row_stride, int B, 
 
 /*
  * Host-only. Workspace bytes tree_spec_sample needs: two arrays of B * (T + 1) * ceil(V / 4096)
- * doubles (chunk sums of the residual masses) and B arrival counters of the workgroups that
- * share a sequence's row passes.
+ * doubles (chunk sums of the residual masses; the second is where the workgroups that share a
+ * sequence's row passes exchange theirs).
  */
 int tree_spec_sample_workspace_size(int B, int T, int V, size_t *bytes);
 

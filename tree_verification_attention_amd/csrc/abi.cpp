@@ -396,11 +396,11 @@ static int check_spec(int B, int T, int V) {
     return TA_OK;
 }
 
-// Workspace of tree_spec_sample: mass chunk sums, pass chunk sums (both B (T + 1) nch doubles),
-// then B arrival counters.
+// Workspace of tree_spec_sample: mass chunk sums, then the walk's pass chunk sums (both
+// B (T + 1) nch doubles).
 static size_t spec_ws_bytes(int B, int T, int V) {
     const size_t n = (size_t)B * (T + 1) * ta::spec_sample_chunks(V);
-    return align256(2 * n * sizeof(double) + (size_t)B * sizeof(uint32_t));
+    return align256(2 * n * sizeof(double));
 }
 
 int tree_spec_sample_workspace_size(int B, int T, int V, size_t *bytes) {
@@ -427,8 +427,7 @@ int tree_spec_sample(const float *p, const float *q, int64_t row_stride, int B, 
     const size_t n = (size_t)B * (T + 1) * ta::spec_sample_chunks(V);
     double *sums = static_cast<double *>(ws);
     ta::SpecArgs a{p, q, row_stride, B, T, V, draft, parent, u_accept, u_sample, sums, sums + n,
-                   reinterpret_cast<uint32_t *>(sums + 2 * n), accept_len, path, next_token,
-                   err_flag};
+                   accept_len, path, next_token, err_flag};
     return status(ta::launch_spec_sample(a, cu_count(), stream));
 }
 

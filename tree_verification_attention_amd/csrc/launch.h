@@ -110,7 +110,6 @@ struct SpecArgs {
     const double *u_sample;  // [B]
     double *sums;            // workspace: [B * (T + 1)][nch] chunk sums of the mass kernel
     double *pass_sums;       // workspace: [B][T + 1][nch] chunk sums of the walk's row passes
-    uint32_t *counters;      // workspace: [B] arrival counters of the walk's workgroups
     int32_t *accept_len, *path, *next_token, *err;
 };
 

@@ -70,12 +70,11 @@ __device__ inline bool position_has_child(const int32_t *parent, int T, int pos)
 __global__ __launch_bounds__(kMassThreads) void spec_mass_kernel(const float *p, const float *q,
                                                                  int64_t row_stride, int T, int V,
                                                                  int nch, const int32_t *parent,
-                                                                 double *sums, uint32_t *counters,
-                                                                 int B) {
+                                                                 double *sums, double *pass_sums) {
     const int chunk = blockIdx.x;
-    if (chunk == 0 && blockIdx.y == 0)  // the walk's arrival counters start at zero
-        for (int i = threadIdx.x; i < B; i += kMassThreads) counters[i] = 0u;
     const int row_id = blockIdx.y;  // b * (T + 1) + row
+    // the walk's pass slots (as many as chunk sums here) start empty
+    if (threadIdx.x == 0) pass_sums[(int64_t)row_id * nch + chunk] = -1.0;
     const int b = row_id / (T + 1), row = row_id % (T + 1);
     // rows of positions without children are never needed here: a bonus token's weights come
     // from a pass of the walk over the one row it ends on
@@ -121,7 +120,7 @@ struct WalkShared {
     double red[kWalkThreads / 64];
     int32_t path[TA_MAX_TREE];
     // walk state (written by thread 0; every workgroup of a sequence holds the same)
-    int32_t pos, child, k, n_path, have_pass, done, bonus, n_pass, pass_ok, pass_q;
+    int32_t pos, child, k, n_path, have_pass, done, bonus, n_pass, pass_q;
     double Cprev, Nk, pass_C, pass_N, theta, base;
     int32_t pass_row, chunk_hit;
 };
@@ -155,10 +154,11 @@ __device__ inline double chunk_sum_block(const float *pr, const float *qr, doubl
 }
 
 // One sequence is walked by G workgroups (blockIdx.x = g). They hold identical walk state and
-// take identical decisions; a row pass is split between them (chunk c by workgroup c mod G),
-// its chunk sums meet in the workspace, and a counter per sequence tells when all have arrived.
-// A workgroup that waits too long (its peers not resident) computes the missing chunks itself
-// with the same arithmetic, so the decisions never depend on the schedule.
+// take identical decisions; a row pass is split between them (chunk c by workgroup c mod G) and
+// its chunk sums meet in fresh workspace slots that start at -1, each reader polling a slot
+// until its owner has filled it. A workgroup that waits too long (its peers not resident)
+// computes the missing chunks itself with the same arithmetic, so the decisions never depend on
+// the schedule.
 __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int nch, int G) {
     __shared__ WalkShared sh;
     const float *p = a.p, *q = a.q;
@@ -293,35 +293,25 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int
         for (int ch = g; ch < nch; ch += G) {
             const double s = chunk_sum_block(p + ro, q + ro, C, pq, ch, nch, V, sh.red);
             if (tid == 0) {
-                buf[ch] = s;
+                __hip_atomic_store(buf + ch, s, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
                 sh.cs[ch] = s;
             }
         }
-        if (tid == 0) {
-            int ok = 1;
-            if (G > 1) {
-                __threadfence();
-                atomicAdd(a.counters + b, 1u);
-                const unsigned target = (unsigned)(pass + 1) * (unsigned)G;
-                for (int spin = 0;; ++spin) {
-                    if (__hip_atomic_load(a.counters + b, __ATOMIC_ACQUIRE,
-                                          __HIP_MEMORY_SCOPE_AGENT) >= target)
-                        break;
-                    if (spin >= kSpinLimit) {
-                        ok = 0;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-                }
+        // the peers' chunks: a thread per chunk polls its slot until the owner has written it
+        // (the mass kernel set every slot to -1; sums are >= 0)
+        bool late = false;
+        for (int ch = tid; ch < nch; ch += kWalkThreads) {
+            if (ch % G == g) continue;
+            double v = __hip_atomic_load(buf + ch, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+            for (int spin = 0; v < 0.0 && spin < kSpinLimit; ++spin) {
+                __builtin_amdgcn_s_sleep(2);
+                v = __hip_atomic_load(buf + ch, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
             }
-            sh.pass_ok = ok;
+            if (v < 0.0) late = true;
+            else sh.cs[ch] = v;
         }
-        __syncthreads();
-        if (sh.pass_ok) {
-            for (int ch = tid; ch < nch; ch += kWalkThreads)
-                if (ch % G != g)
-                    sh.cs[ch] = __hip_atomic_load(buf + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
+        if (__syncthreads_or(late)) {
+            // peers not resident: every other chunk here, with the same arithmetic
             for (int ch = 0; ch < nch; ++ch)
                 if (ch % G != g) {
                     const double s = chunk_sum_block(p + ro, q + ro, C, pq, ch, nch, V, sh.red);
@@ -469,7 +459,7 @@ hipError_t launch_spec_sample(const SpecArgs &a, int cus, hipStream_t s) {
     int G = cus / (a.B > 0 ? a.B : 1);
     G = G < 1 ? 1 : (G > nch ? nch : G);
     hipLaunchKernelGGL(spec_mass_kernel, dim3(nch, a.B * (a.T + 1)), dim3(kMassThreads), 0, s, a.p,
-                       a.q, a.row_stride, a.T, a.V, nch, a.parent, a.sums, a.counters, a.B);
+                       a.q, a.row_stride, a.T, a.V, nch, a.parent, a.sums, a.pass_sums);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(spec_walk_kernel, dim3(G, a.B), dim3(kWalkThreads), 0, s, a, nch, G);
