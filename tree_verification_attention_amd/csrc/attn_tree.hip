@@ -112,8 +112,8 @@ __global__ __launch_bounds__(NW * 64) void attn_tree_kernel(AttnArgs a) {
     if (has_tree) {
         AncestorLds &anc = *reinterpret_cast<AncestorLds *>(smem);
         const int cur = build_ancestor_masks(a.parent + (int64_t)b * a.T, a.T, anc, a.err, tid, NT);
-        for (int e = tid; e < a.T * kMaskWords; e += NT)
-            node_mask[e / kMaskWords][e % kMaskWords] = anc.m[cur][e / kMaskWords][e % kMaskWords];
+        const int W = (a.T + 63) >> 6;
+        for (int e = tid; e < a.T * W; e += NT) node_mask[e / W][e % W] = anc.m[cur][e / W][e % W];
     }
     __syncthreads();  // page cache and masks visible; the tile stages reuse the mask scratch
 
