@@ -44,9 +44,13 @@ CSRC = os.path.join(ROOT, "tree_verification_attention_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+# the sources of the two kernels the traffic counters cover
+TRAFFIC_SOURCES = ("attn_prefix.hip", "attn_tree.hip", "lds_dma.h", "ancestors.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    for path in sorted(os.path.join(CSRC, n) for n in TRAFFIC_SOURCES):
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode())
             h.update(f.read())
