@@ -178,6 +178,49 @@ def make_evict():
     return lambda: torch.sum(buf, dim=0, out=out)
 
 
+def time_breakdown(case, steps, warmup):
+    """The unfused entry points on the same layer, each call timed alone with HIP events after an
+    evicting read: mask build, prefix part (its splits merged), tree part, two-way merge."""
+    import torch
+
+    from tree_verification_attention_amd import _lib
+
+    g = to_device(case)
+    evict = make_evict()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(steps):
+            evict()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return round(statistics.median(a.elapsed_time(b) * 1e3 for a, b in evs), 2)
+
+    kw = dict(scale=case.scale)
+    oc, lc = _lib.prefix(g["q"], g["k_cache"], g["v_cache"], g["seq_lens"], **kw)
+    os_, ls = _lib.tree(g["q"], g["k_tree"], g["v_tree"], g["parent"], **kw)
+    out = {
+        "mask_build_us": timed(lambda: _lib.mask_build(g["parent"])),
+        "prefix_us": timed(lambda: _lib.prefix(g["q"], g["k_cache"], g["v_cache"], g["seq_lens"],
+                                               **kw)),
+        "tree_us": timed(lambda: _lib.tree(g["q"], g["k_tree"], g["v_tree"], g["parent"], **kw)),
+        "merge_us": timed(lambda: _lib.merge(oc, lc, os_, ls, out_dtype=torch.bfloat16)),
+        "note": "unfused entry points, each call timed alone (median) after an evicting read; "
+                "the prefix call includes the merge of its own splits",
+    }
+    del g, oc, lc, os_, ls
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_next_rows(steps, warmup, seed):
     """Greedy tree acceptance over a Llama-3-size vocabulary and the accepted-path KV commit, at
     the headline batch / tree / head shape; each call timed with HIP events after a cache-evicting read."""
@@ -676,6 +719,8 @@ def main():
     }
     torch.cuda.empty_cache()
     if not args.no_secondary and wl.name == "gqa_64k_pinned":
+        print("[bench] unfused breakdown", file=sys.stderr, flush=True)
+        line["breakdown"] = time_breakdown(case, max(5, args.steps // 5), 3)
         wl2 = inputs.WORKLOADS["gqa_64k"]
         case2 = inputs.make_case(wl2, args.seed, pad="finite")
         w2 = work_of(case2)
