@@ -305,6 +305,15 @@ def time_next_rows(steps, warmup, seed):
     t0 = time.perf_counter()
     ogdn.gdn_tree_verify(gc.q, gc.k, gc.v, gc.g, gc.beta, gc.parent, gc.S0, gc.scale)
     gdn_cpu_s = time.perf_counter() - t0
+    # the deferred commit: the committed states take the accepted path's updates (in place; a
+    # repeated call keeps applying them, which changes the values, not the work)
+    gpath, gn = inputs.random_paths(gc.parent, np.random.default_rng(seed + 1))
+    gpath_d, gn_d = torch.from_numpy(gpath).cuda(), torch.from_numpy(gn).cuda()
+    gS = gs0.clone()
+    print("[bench] GDN deferred commit", file=sys.stderr, flush=True)
+    gcom_us = timed(lambda: _lib.gdn_commit(gk, gv, gg, gb, gpath_d, gn_d, gS))
+    # states read and written once, plus each accepted node's key, value, decay and beta
+    gcom_bytes = 2 * gc.S0.nbytes + int(gn.sum()) * (GHk * Gd * 2 + GHv * Gd * 2 + GHv * 8) + 4 * B
 
     wl = inputs.Workload("commit", B=B, Hq=32, Hkv=8, D=128, T=T, L=4096)
     cc = inputs.make_case(wl, seed, pad="finite", lcap=4096 + T)
@@ -342,6 +351,13 @@ def time_next_rows(steps, warmup, seed):
             "peak_tflops": 157.3, "bound": "alu (fp32)",
             "frac": round(gdn_flops / (gdn_us * 1e-6) / 1e12 / 157.3, 4),
             "bytes": gdn_bytes, "cpu_oracle_s": round(gdn_cpu_s, 3)},
+        "gdn_commit": {
+            "workload": f"B={B}, H_v={GHv}, d_k=d_v={Gd} fp32 states, {int(gn.sum())} accepted "
+                        "nodes in all",
+            "us": round(gcom_us, 2), "algorithmic_bytes": gcom_bytes,
+            "achieved_gbs": round(gcom_bytes / (gcom_us * 1e-6) / 1e9, 1),
+            "peak_gbs": HBM_PEAK_GBS,
+            "frac": round(gcom_bytes / (gcom_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "kv_commit": {
             "workload": f"B={B}, Hkv=8, D=128 bf16, contiguous cache, {int(n.sum())} rows committed",
             "us": round(com_us, 2), "algorithmic_bytes": com_bytes,
@@ -532,7 +548,8 @@ def accept_stats_summary(stats_dir, steps):
     lines = [
         "# rocprofv3 kernel statistics, greedy tree acceptance (B=4, T=64, vocab 128256, bf16 "
         "logits), tree speculative sampling (same tree and vocabulary, fp32 p and q), GDN tree "
-        "verification (B=4, T=128, H_k=16, H_v=32, d_k=d_v=128) and accepted-path KV commit "
+        "verification (B=4, T=128, H_k=16, H_v=32, d_k=d_v=128) with its deferred state commit, and "
+        "accepted-path KV commit "
         "(B=4, Hkv=8, D=128 bf16)",
         f"# command: rocprofv3 --kernel-trace --stats -d STATS_DIR -o run --output-format csv -- "
         f"python3 bench.py --next-rows-only --steps {steps} --warmup 5",

@@ -101,3 +101,24 @@ def test_gdn_commit_bad_path_sets_flag():
     torch.cuda.synchronize()
     assert int(err.item()) & _lib.TA_DEV_BAD_COMMIT
     np.testing.assert_array_equal(S.cpu().numpy()[1], c.S0[1])   # accept_len 9 > T: unchanged
+    # sequence 0 stops at the invalid entry: its state is node 0's
+    ref = G.gdn_commit(c.q, c.k, c.v, c.g, c.beta, c.parent, c.S0, np.array([0, -1]))
+    assert np.abs(S.cpu().numpy()[0] - ref[0]).max() <= TOL
+
+
+def test_gdn_commit_stops_mid_path():
+    """An invalid entry past the first 32 path steps: the updates before it (across a staging
+    boundary) are applied, the rest are not."""
+    c = inputs.make_gdn_case(2, 64, 2, 4, 128, 64, 5, tree="chain")
+    path = np.tile(np.arange(64, dtype=np.int32), (2, 1))
+    path[0, 40] = 99
+    n = np.array([64, 37], np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    S = dev(c.S0)
+    _lib.gdn_commit(dev(c.k), dev(c.v), dev(c.g), dev(c.beta), dev(path), dev(n), S, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & _lib.TA_DEV_BAD_COMMIT
+    ref = G.gdn_commit(c.q, c.k, c.v, c.g, c.beta, c.parent, c.S0, np.array([39, 36]))
+    d = np.abs(S.cpu().numpy() - ref).max()
+    say(f"stops_mid_path: max|dS| {d:.3e}")
+    assert d <= TOL

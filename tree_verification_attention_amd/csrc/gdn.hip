@@ -387,72 +387,124 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
 }
 
 // Deferred commit: S <- the state after the updates of path[b][0 .. n-1] (root first), for one
-// (32-column block, value head, sequence). Thread (d, c-group) owns S[d][4 c-group .. +3].
+// (32-column block, value head, sequence). Thread (d, c-group) owns S[d][4 c-group .. +3]. The
+// path is taken kCommitStage steps at a time: the steps' key rows, value columns, decays and
+// betas are first staged in LDS together (one round trip to memory for all of them), then the
+// updates run back to back with one barrier each.
+constexpr int kCommitStage = 32;
+
 template <int DK>
 __global__ __launch_bounds__(kGdnThreads) void gdn_commit_kernel(GdnCommitArgs a) {
     const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int hk = h / (a.Hv / a.Hk), c0 = cb * kColBlock;
     constexpr int kRowsPerPass = kGdnThreads / (kColBlock / 4);  // 32 rows of S per pass
     constexpr int kPasses = DK / kRowsPerPass;
+    constexpr int KCH = DK / 8;                                  // 16-byte chunks of a key row
     const int cg = tid % (kColBlock / 4), r0 = tid / (kColBlock / 4);
-    __shared__ float kt[DK];
-    __shared__ float part[kRowsPerPass][kColBlock];
-    __shared__ float ktS[kColBlock];
+    __shared__ __attribute__((aligned(16))) uint16_t kst[kCommitStage][DK];
+    __shared__ __attribute__((aligned(16))) float vst[kCommitStage][kColBlock];
+    __shared__ float alst[kCommitStage], btst[kCommitStage];
+    __shared__ int32_t tst[kCommitStage];
+    __shared__ int32_t n_ok;
+    // per-wavefront k^T S partial sums, double-buffered so that one barrier per step suffices
+    constexpr int kWaves = kGdnThreads / 64;
+    __shared__ __attribute__((aligned(16))) float part[2][kWaves][kColBlock];
+    // the accepted length, the state and the first path entries are loaded together
     const int n = a.accept_len[b];
-    if (n < 0 || n > a.T) {
-        if (tid == 0 && a.err) atomicOr(a.err, (int32_t)TA_DEV_BAD_COMMIT);
-        return;
-    }
     float *Sg = a.S + ((int64_t)b * a.Hv + h) * DK * a.dv;
     float4 S[kPasses];
 #pragma unroll
     for (int p = 0; p < kPasses; ++p)
         S[p] = *reinterpret_cast<const float4 *>(Sg + (int64_t)(r0 + p * kRowsPerPass) * a.dv + c0 +
                                                  4 * cg);
+    const int t_first = tid < min(kCommitStage, a.T) ? a.path[(int64_t)b * a.T + tid] : 0;
+    if (n < 0 || n > a.T) {
+        if (tid == 0 && a.err) atomicOr(a.err, (int32_t)TA_DEV_BAD_COMMIT);
+        return;
+    }
     const uint16_t *kg = static_cast<const uint16_t *>(a.k);
     const uint16_t *vg = static_cast<const uint16_t *>(a.v);
-    for (int s = 0; s < n; ++s) {
-        const int t = a.path[(int64_t)b * a.T + s];
-        if (t < 0 || t >= a.T) {
+    int step = 0;
+    for (int s0 = 0; s0 < n; s0 += kCommitStage) {
+        const int m = min(kCommitStage, n - s0);
+        if (tid == 0) n_ok = m;
+        __syncthreads();  // n_ok set; the previous chunk's staged operands are no longer read
+        if (tid < m) {
+            const int t = s0 == 0 ? t_first : a.path[(int64_t)b * a.T + s0 + tid];
+            const bool ok = t >= 0 && t < a.T;
+            if (!ok) atomicMin(&n_ok, tid);
+            tst[tid] = ok ? t : 0;
+        }
+        __syncthreads();
+        const int mg = n_ok;  // the chunk's steps before its first invalid entry
+        for (int e = tid; e < mg * KCH; e += kGdnThreads) {
+            const int st = e / KCH, c = e % KCH;
+            *reinterpret_cast<uint4 *>(&kst[st][8 * c]) = *reinterpret_cast<const uint4 *>(
+                kg + (((int64_t)b * a.T + tst[st]) * a.Hk + hk) * DK + 8 * c);
+        }
+        for (int e = tid; e < mg * (kColBlock / 4); e += kGdnThreads) {
+            const int st = e / (kColBlock / 4), c = e % (kColBlock / 4);
+            const uint2 w = *reinterpret_cast<const uint2 *>(
+                vg + (((int64_t)b * a.T + tst[st]) * a.Hv + h) * a.dv + c0 + 4 * c);
+            *reinterpret_cast<float4 *>(&vst[st][4 * c]) =
+                make_float4(bf((uint16_t)w.x), bf((uint16_t)(w.x >> 16)), bf((uint16_t)w.y),
+                            bf((uint16_t)(w.y >> 16)));
+        }
+        if (tid < mg) {
+            const int64_t gi = ((int64_t)b * a.T + tst[tid]) * a.Hv + h;
+            alst[tid] = __expf(a.g[gi]);
+            btst[tid] = a.beta[gi];
+        }
+        __syncthreads();
+        for (int st = 0; st < mg; ++st, ++step) {
+            float(*pt)[kColBlock] = part[step & 1];
+            float kd[kPasses];
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) kd[p] = bf(kst[st][r0 + p * kRowsPerPass]);
+            // k^T S for this column block
+            float4 acc = make_float4(0, 0, 0, 0);
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                acc.x = fmaf(kd[p], S[p].x, acc.x);
+                acc.y = fmaf(kd[p], S[p].y, acc.y);
+                acc.z = fmaf(kd[p], S[p].z, acc.z);
+                acc.w = fmaf(kd[p], S[p].w, acc.w);
+            }
+            // over the wavefront's 8 row groups (lanes cg, cg + 8, ..., cg + 56), then over the
+            // wavefronts
+#pragma unroll
+            for (int o = 8; o < 64; o <<= 1) {
+                acc.x += __shfl_xor(acc.x, o);
+                acc.y += __shfl_xor(acc.y, o);
+                acc.z += __shfl_xor(acc.z, o);
+                acc.w += __shfl_xor(acc.w, o);
+            }
+            if ((tid & 63) < kColBlock / 4) *reinterpret_cast<float4 *>(&pt[tid >> 6][4 * cg]) = acc;
+            __syncthreads();
+            float4 ks = make_float4(0, 0, 0, 0);
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float4 x = *reinterpret_cast<const float4 *>(&pt[w][4 * cg]);
+                ks.x += x.x;
+                ks.y += x.y;
+                ks.z += x.z;
+                ks.w += x.w;
+            }
+            const float al = alst[st], bt = btst[st];
+            const float4 v = *reinterpret_cast<const float4 *>(&vst[st][4 * cg]);
+#pragma unroll
+            for (int p = 0; p < kPasses; ++p) {
+                // S = a (S - b k (k^T S)) + b k v^T
+                S[p].x = al * (S[p].x - bt * kd[p] * ks.x) + bt * kd[p] * v.x;
+                S[p].y = al * (S[p].y - bt * kd[p] * ks.y) + bt * kd[p] * v.y;
+                S[p].z = al * (S[p].z - bt * kd[p] * ks.z) + bt * kd[p] * v.z;
+                S[p].w = al * (S[p].w - bt * kd[p] * ks.w) + bt * kd[p] * v.w;
+            }
+        }
+        if (mg < m) {
             if (tid == 0 && a.err) atomicOr(a.err, (int32_t)TA_DEV_BAD_COMMIT);
-            break;  // uniform: every thread reads the same entry
+            break;  // uniform: every thread read the same n_ok
         }
-        for (int d = tid; d < DK; d += kGdnThreads)
-            kt[d] = bf(kg[(((int64_t)b * a.T + t) * a.Hk + hk) * DK + d]);
-        __syncthreads();
-        // k^T S for this column block
-        float4 acc = make_float4(0, 0, 0, 0);
-#pragma unroll
-        for (int p = 0; p < kPasses; ++p) {
-            const float kd = kt[r0 + p * kRowsPerPass];
-            acc.x = fmaf(kd, S[p].x, acc.x);
-            acc.y = fmaf(kd, S[p].y, acc.y);
-            acc.z = fmaf(kd, S[p].z, acc.z);
-            acc.w = fmaf(kd, S[p].w, acc.w);
-        }
-        *reinterpret_cast<float4 *>(&part[r0][4 * cg]) = acc;
-        __syncthreads();
-        if (tid < kColBlock) {
-            float sum = 0.f;
-            for (int r = 0; r < kRowsPerPass; ++r) sum += part[r][tid];
-            ktS[tid] = sum;
-        }
-        __syncthreads();
-        const float al = __expf(a.g[((int64_t)b * a.T + t) * a.Hv + h]);
-        const float bt = a.beta[((int64_t)b * a.T + t) * a.Hv + h];
-        const uint16_t *vr = vg + (((int64_t)b * a.T + t) * a.Hv + h) * a.dv + c0 + 4 * cg;
-        const float v0 = bf(vr[0]), v1 = bf(vr[1]), v2 = bf(vr[2]), v3 = bf(vr[3]);
-        const float4 ks = *reinterpret_cast<const float4 *>(&ktS[4 * cg]);
-#pragma unroll
-        for (int p = 0; p < kPasses; ++p) {
-            const float kd = kt[r0 + p * kRowsPerPass];
-            // S = a (S - b k (k^T S)) + b k v^T
-            S[p].x = al * (S[p].x - bt * kd * ks.x) + bt * kd * v0;
-            S[p].y = al * (S[p].y - bt * kd * ks.y) + bt * kd * v1;
-            S[p].z = al * (S[p].z - bt * kd * ks.z) + bt * kd * v2;
-            S[p].w = al * (S[p].w - bt * kd * ks.w) + bt * kd * v3;
-        }
-        __syncthreads();  // kt / part / ktS are rewritten by the next step
     }
 #pragma unroll
     for (int p = 0; p < kPasses; ++p)
