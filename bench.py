@@ -11,8 +11,9 @@ A step is one call of tree_attn_forward: all prefix splits plus the masked tree 
 log-sum-exp combine. ``value`` is the achieved algorithmic HBM bandwidth of a step (prefix K/V,
 Q, tree K/V and parents read once; O and LSE written once) in TB/s; ``us_per_layer`` is the
 same step's time. The roofline entry is for the split step that carries all the HBM traffic:
-one tree_attn_partials call (the prefix kernel, plus the small masked kernel for the tree and
-the prefix tail), launched alone and timed with HIP events on its stream.
+one tree_attn_partials call (one prefix-kernel launch; its last split also takes the masked
+part, the tree keys and the prefix tail), launched alone and timed with HIP events on its
+stream.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --parse-pmc FETCH_DIR WRITE_DIR   (writes the traffic summary)
@@ -37,7 +38,6 @@ METRIC = "tree-verify attention µs/layer + achieved HBM TB/s, 64-node tree @64k
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 KERNEL_NAME = "attn_prefix_kernel"
-TREE_KERNEL_NAME = "attn_tree_kernel"
 COPY_BYTES = 1 << 30
 FLUSH_BYTES = 1 << 29
 CSRC = os.path.join(ROOT, "tree_verification_attention_amd", "csrc")
@@ -45,7 +45,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 # the sources of the two kernels the traffic counters cover
-TRAFFIC_SOURCES = ("attn_prefix.hip", "attn_tree.hip", "lds_dma.h", "ancestors.h")
+TRAFFIC_SOURCES = ("attn_prefix.hip", "lds_dma.h", "ancestors.h", "launch.h", "abi.cpp")
 
 
 def kernel_source_hash() -> str:
@@ -477,12 +477,12 @@ def parse_pmc(fetch_dir, write_dir, workload):
         return out
 
     def kernel(vals):
-        # one tree_attn_partials call = one prefix-kernel and one tree-kernel dispatch
+        # one tree_attn_partials call = one prefix-kernel dispatch (the masked part rides on
+        # its last split)
         xs = [v for k, v in vals if KERNEL_NAME in k]
-        ys = [v for k, v in vals if TREE_KERNEL_NAME in k]
-        if not xs or not ys:
-            raise SystemExit(f"no dispatches of {KERNEL_NAME} / {TREE_KERNEL_NAME} in the counters")
-        return statistics.mean(xs) + statistics.mean(ys), len(xs), next(k for k, _ in vals if KERNEL_NAME in k)
+        if not xs:
+            raise SystemExit(f"no dispatches of {KERNEL_NAME} in the counters")
+        return statistics.mean(xs), len(xs), next(k for k, _ in vals if KERNEL_NAME in k)
 
     def copy(vals):
         # the 1 GiB calibration copies: the largest copy dispatches (input uploads are tiny)
@@ -512,8 +512,8 @@ def parse_pmc(fetch_dir, write_dir, workload):
     run = (f"python3 bench.py --workload {workload} --steps 4 --warmup 1 --no-secondary "
            f"--no-cpu-baseline --no-next-rows --copy-calibration")
     with open(out, "w") as f:
-        f.write(f"# HBM traffic of one tree_attn_partials call ({KERNEL_NAME} + {TREE_KERNEL_NAME} "
-                f"dispatch) on workload {workload}.\n"
+        f.write(f"# HBM traffic of one tree_attn_partials call (one {KERNEL_NAME} dispatch: the "
+                f"prefix splits and the masked part) on workload {workload}.\n"
                 f"# FETCH pass: rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- {run}\n"
                 f"# WRITE pass: rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR -o run --output-format csv -- {run}\n"
                 f"# summary:    python3 bench.py --workload {workload} --parse-pmc FETCH_DIR WRITE_DIR\n"
@@ -591,10 +591,9 @@ def stats_summary(stats_dir, workload, steps):
     def durs_of(name):
         return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
                 for r in trace if name in r["Kernel_Name"]]
-    durs, tdurs = durs_of(KERNEL_NAME), durs_of(TREE_KERNEL_NAME)
+    durs = durs_of(KERNEL_NAME)
     alone = durs[-steps:]            # the kernel-alone loop: the last `steps` launches
     fused = durs[:-steps][-steps:]   # the timed fused loop before it
-    talone = tdurs[-steps:]
     bench_avg = None
     logs = glob.glob(os.path.join(os.path.dirname(stats_dir.rstrip("/")),
                                   os.path.basename(stats_dir.rstrip("/")) + ".log"))
@@ -621,8 +620,8 @@ def stats_summary(stats_dir, workload, steps):
         f"average {statistics.mean(fused):.2f} us",
         f"{KERNEL_NAME}, kernel-alone loop ({len(alone)} launches, 512 MiB evicting read before each): "
         f"average {statistics.mean(alone):.2f} us, median {statistics.median(alone):.2f} us",
-        f"{TREE_KERNEL_NAME}, same loop: average {statistics.mean(talone):.2f} us",
-        f"sum per tree_attn_partials call: {statistics.mean(alone) + statistics.mean(talone):.2f} us",
+        f"one {KERNEL_NAME} dispatch per tree_attn_partials call (the masked part rides on the "
+        f"last split)",
         f"bench.py kernel_avg_us (HIP events around the same tree_attn_partials calls): {bench_avg}",
     ]
     with open(out, "w") as f:
@@ -726,7 +725,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic["traffic_bytes"] if traffic else None,
-                     "kernel": f"{KERNEL_NAME} + {TREE_KERNEL_NAME} (tree_attn_partials)",
+                     "kernel": f"{KERNEL_NAME} (tree_attn_partials: the prefix splits and, on "
+                               f"the last split, the masked part)",
                      "kernel_avg_us": round(kern_avg_us, 2),
                      "kernel_bytes": work["kernel_bytes"]},
         "mfma": {"achieved_tflops": round(work["flops"] / (kern_avg_us * 1e-6) / 1e12, 1),

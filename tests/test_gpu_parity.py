@@ -157,6 +157,36 @@ def test_unfused_calls_and_merge():
     np.testing.assert_allclose(l_x.cpu().numpy().reshape(-1), ref[1], atol=1e-5)
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_fused_tree_part_matches_tree_call(layout):
+    """tree_attn_partials computes the masked part in the prefix launch (the last split's
+    workgroups go on with it). With prefix lengths of whole 64-key tiles there is no tail, so
+    that part must equal what tree_attn_tree returns, bit for bit: the same per-row arithmetic
+    over the same tree tiles. Several row blocks, D = 64 and 128."""
+    for D, T, Hq, Hkv in ((128, 64, 8, 2), (64, 40, 4, 4), (128, 100, 10, 2)):
+        w = wl(B=3, Hq=Hq, Hkv=Hkv, D=D, T=T, L=(130, 900))
+        case = inputs.make_case(w, 5, layout=layout, page_size=16 if D == 64 else 64)
+        case.seq_lens[:] = (case.seq_lens // 64) * 64
+        case.seq_lens[0] = 0                      # an empty prefix rides along too
+        g = to_gpu(case)
+        p = _lib.make_problem(g["q"], g["k_cache"], g["v_cache"], g["seq_lens"], g["k_tree"],
+                              g["v_tree"], g["parent"], block_table=g["block_table"],
+                              page_size=g["page_size"], scale=case.scale)
+        ws = torch.empty(_lib.workspace_size(p), dtype=torch.uint8, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        _lib.partials(p, ws, err=err)
+        o_s, l_s = _lib.tree(g["q"], g["k_tree"], g["v_tree"], g["parent"], scale=case.scale)
+        torch.cuda.synchronize()
+        n, rows = _lib.num_splits(p), 3 * T * Hq
+        o_part = ws[:(n + 1) * rows * D * 4].view(torch.float32).view(n + 1, rows, D)[n]
+        off = _lib.workspace_lse_offset(p)
+        l_part = ws[off:off + (n + 1) * rows * 4].view(torch.float32).view(n + 1, rows)[n]
+        say(f"fused masked part D={D} T={T} {layout}: {n} splits, lens {case.seq_lens.tolist()}")
+        assert int(err.item()) == 0
+        assert torch.equal(o_part, o_s.view(rows, D)), "O of the masked part differs"
+        assert torch.equal(l_part, l_s.view(rows)), "LSE of the masked part differs"
+
+
 def test_merge_degenerate_parts():
     sh = (1, 3, 2)
     o_a = torch.randn(*sh, 64, device="cuda")

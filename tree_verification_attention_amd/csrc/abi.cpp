@@ -128,7 +128,14 @@ Plan make_plan(const ta_problem *p) {
         if (want > most) want = most;
         n = want < 1 ? 1 : (int)want;
     }
-    int64_t chunk = pl.capacity > 0 ? ((int64_t)pl.capacity + n - 1) / n : 1;
+    // bf16: the last split also runs the masked part (the tail tile, the tree tiles and the
+    // mask build, about ceil(T / 64) + 2 tiles of time), so unless the caller fixed the split
+    // count the chunks are sized as if the prefix were that much longer, which leaves the last
+    // split correspondingly short
+    const int64_t reserve = p->dtype == TA_BF16 && p->num_splits == 0
+                                ? (int64_t)ta::kKeyTile * ((p->T + ta::kKeyTile - 1) / ta::kKeyTile + 2)
+                                : 0;
+    int64_t chunk = pl.capacity > 0 ? ((int64_t)pl.capacity + reserve + n - 1) / n : 1;
     chunk = (chunk + ta::kKeyTile - 1) / ta::kKeyTile * ta::kKeyTile;
     if (p->block_table && p->dtype == TA_BF16) {
         // a part's block-table entries are cached in LDS (kPageCache of them)
@@ -184,11 +191,14 @@ AttnArgs make_args(const ta_problem *p, const Plan &pl, int32_t *err) {
 int status(hipError_t e) { return e == hipSuccess ? TA_OK : TA_EHIP; }
 
 // The prefix splits into parts 0 .. n_splits - 1 of (wo, wl) (bf16: full 64-key tiles only).
+// With ``tree`` (bf16 only), the last split's workgroups go on with the masked part -- the prefix
+// keys past the last full tile and the tree keys -- into part n_splits, in the same launch.
 int launch_prefix_parts(const ta_problem *p, const Plan &pl, int32_t *err, float *wo, float *wl,
-                        hipStream_t s) {
+                        bool tree, hipStream_t s) {
     AttnArgs a = make_args(p, pl, err);
     a.n_splits = pl.n_splits;
     a.with_prefix = 1;
+    a.with_tree = tree && p->dtype == TA_BF16;
     a.out_o = wo;
     a.out_lse = wl;
     a.part_so = pl.rows * p->D;
@@ -266,7 +276,7 @@ int tree_attn_prefix(const ta_problem *p, float *o_c, float *lse_c, void *ws, si
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
     float *wo = static_cast<float *>(ws);
     float *wl = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
-    if ((rc = launch_prefix_parts(p, pl, err_flag, wo, wl, stream))) return rc;
+    if ((rc = launch_prefix_parts(p, pl, err_flag, wo, wl, false, stream))) return rc;
     int parts = pl.n_splits;
     if (p->dtype == TA_BF16) {
         // the prefix keys past the last full tile, as one more part
@@ -322,7 +332,8 @@ int tree_attn_partials(const ta_problem *p, void *ws, size_t ws_bytes, int32_t *
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
     float *wo = static_cast<float *>(ws);
     float *wl = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
-    if ((rc = launch_prefix_parts(p, pl, err_flag, wo, wl, stream))) return rc;
+    if ((rc = launch_prefix_parts(p, pl, err_flag, wo, wl, true, stream))) return rc;
+    if (p->dtype == TA_BF16) return TA_OK;  // the masked part rode with the last split
     return launch_last_part(p, pl, err_flag, wo + pl.n_splits * pl.rows * p->D,
                             wl + pl.n_splits * pl.rows, true, true, stream);
 }

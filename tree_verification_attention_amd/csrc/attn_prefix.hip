@@ -3,10 +3,13 @@
 // The cache part of LongSpec's Hybrid Tree Attention needs no mask: every draft-tree node sees
 // the whole committed prefix of its sequence (LongSpec page, "Fast tree attention"). This kernel
 // computes it over the prefix's full 64-key tiles, split along the prefix so that every compute
-// unit streams its own slice; the keys past the last full tile (fewer than 64) are left to the
-// masked tree kernel, and all parts are combined afterwards by the log-sum-exp identity of the
-// same section (merge kernel). With no mask, no ragged tile and no tree, the loop holds nothing
-// but the streaming and the two products.
+// unit streams its own slice. The keys past the last full tile (fewer than 64) and the tree's
+// own keys form the masked part: when the tree rides along (tree_attn_partials / forward), the
+// last split's workgroups -- sized a few tiles short for it -- take it after their prefix tiles,
+// under the ancestor-or-self mask built in LDS; otherwise the masked tree kernel does. All parts
+// are combined afterwards by the log-sum-exp identity of the same section (merge kernel). The
+// prefix loop itself holds no mask, no ragged tile and no tree: nothing but the streaming and
+// the two products.
 //
 // One workgroup handles one (part, kv-head, row block, sequence). Query packing: the G = Hq / Hkv
 // query heads sharing a KV head and the T tree nodes form R = T * G rows, row = node * G + group
@@ -32,6 +35,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "ancestors.h"
 #include "launch.h"
 #include "lds_dma.h"
 #include "treeattn.h"
@@ -55,6 +59,9 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
 
     __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE_B];
     __shared__ int32_t page_cache[PAGED ? kPageCache : 1];
+    __shared__ uint64_t node_mask[TA_MAX_TREE][kMaskWords];  // masked part only
+    constexpr int SCR = (int)((sizeof(AncestorLds) + STAGE_B - 1) / STAGE_B);  // mask scratch stages
+    static_assert(SCR < NS, "mask scratch must leave a stage for the tiles");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -311,30 +318,194 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
         run_pass(2);
     }
 
-    // ---- normalise and write this part's (O, LSE); register r of O^T tile dt holds
+    // ---- normalise and write a part's (O, LSE); register r of O^T tile dt holds
     // d = dt*32 + 8*(r/4) + 4*hf + r%4
     const int r = row0 + l32;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (r < R) {
-        const int node = r / G, h = g * G + r % G;
-        const int64_t orow = ((int64_t)b * a.T + node) * a.Hq + h;
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float *op = a.out_o + part * a.part_so + orow * D + 4 * hf;
+    auto write_part = [&](int slot) TA_INLINE {
+        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        if (r < R) {
+            const int node = r / G, h = g * G + r % G;
+            const int64_t orow = ((int64_t)b * a.T + node) * a.Hq + h;
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            float *op = a.out_o + slot * a.part_so + orow * D + 4 * hf;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                float4 v;
-                v.x = acc[dt][4 * q4 + 0] * inv;
-                v.y = acc[dt][4 * q4 + 1] * inv;
-                v.z = acc[dt][4 * q4 + 2] * inv;
-                v.w = acc[dt][4 * q4 + 3] * inv;
-                *reinterpret_cast<float4 *>(op + dt * 32 + 8 * q4) = v;
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    float4 v;
+                    v.x = acc[dt][4 * q4 + 0] * inv;
+                    v.y = acc[dt][4 * q4 + 1] * inv;
+                    v.z = acc[dt][4 * q4 + 2] * inv;
+                    v.w = acc[dt][4 * q4 + 3] * inv;
+                    *reinterpret_cast<float4 *>(op + dt * 32 + 8 * q4) = v;
+                }
+            if (hf == 0)
+                a.out_lse[slot * a.part_sl + orow] =
+                    l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+        }
+    };
+    write_part(part);
+
+    // ---- the masked part, when the tree rides with the prefix: the last split (the shortest,
+    // or empty for short sequences) goes on with the prefix keys past the last full tile and the
+    // tree's own keys under the ancestor-or-self mask (LongSpec page, "Fast tree attention"),
+    // into part n_splits. Every masked tile takes the exact path: the running maximum moves to
+    // cover each block and what is accumulated is rescaled.
+    if (!a.with_tree || part != a.n_splits - 1) return;
+    __syncthreads();  // every wavefront is done with the ring
+    const int tb = L & ~(KT - 1);  // the tail: prefix keys [tb, L)
+    const int n_tail = L > tb ? 1 : 0;
+    const int n_mt = n_tail + (a.T + KT - 1) / KT;
+    int tpage0 = 0;
+    if (PAGED && n_tail) {
+        tpage0 = tb >> a.page_shift;
+        const int np = ((L - 1) >> a.page_shift) - tpage0 + 1;
+        const int32_t *btab = a.block_table + (int64_t)b * a.max_blocks + tpage0;
+        for (int i = tid; i < np; i += NT) {
+            int pg = btab[i];
+            if ((unsigned)pg >= (unsigned)a.num_pages) {
+                if (a.err) atomicOr(a.err, (int32_t)TA_DEV_BAD_PAGE);
+                pg = 0;
             }
-        if (hf == 0)
-            a.out_lse[part * a.part_sl + orow] =
-                l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+            page_cache[i] = pg;
+        }
+        __syncthreads();
     }
+    const uint32_t trow = 2u * (uint32_t)a.kt_st;
+    const char *kt_b = reinterpret_cast<const char *>(a.kt) + 2 * (b * a.kt_sb + g * a.kt_sh);
+    const char *vt_b = reinterpret_cast<const char *>(a.vt) + 2 * (b * a.kt_sb + g * a.kt_sh);
+
+    // masked tile t (the tail first, if any, then the tree tiles) into stage st; rows past the
+    // tail (or the tree) are clamped to its last row and masked out of the scores. The three
+    // sources are separate branches (uniform per tile), not selects between their pointers.
+    auto issue_masked = [&](int t, int st) TA_INLINE {
+        const uint32_t sb = smem_lds + (uint32_t)(st * STAGE_B);
+        if (t >= n_tail) {
+            const int k0 = (t - n_tail) * KT;
+            const int last = a.T - 1 - k0;
+            const char *kb = kt_b + (uint64_t)k0 * trow;
+            const char *vb = vt_b + (uint64_t)k0 * trow;
+#pragma unroll
+            for (int i = 0; i < NIW; ++i) {
+                const int j = wave * NIW + i;
+                int row;
+                uint32_t off;
+                tile_load_pos<DCH>(j >= NI, j < NI ? j : j - NI, lane, row, off);
+                load_lds_saddr(j < NI ? kb : vb, (uint32_t)min(row, last) * trow + off, sb + ld_lds(i));
+            }
+        } else if (!PAGED) {
+            const int last = L - 1 - tb;
+            const char *kb = kc_b + (uint64_t)tb * prow;
+            const char *vb = vc_b + (uint64_t)tb * prow;
+#pragma unroll
+            for (int i = 0; i < NIW; ++i) {
+                const int j = wave * NIW + i;
+                int row;
+                uint32_t off;
+                tile_load_pos<DCH>(j >= NI, j < NI ? j : j - NI, lane, row, off);
+                load_lds_saddr(j < NI ? kb : vb, (uint32_t)min(row, last) * prow + off, sb + ld_lds(i));
+            }
+        } else {
+            // one aligned group of at most 16 keys per instruction: a single page
+            const int last = L - 1 - tb;
+#pragma unroll
+            for (int i = 0; i < NIW; ++i) {
+                const int j = wave * NIW + i;
+                int row;
+                uint32_t off;
+                tile_load_pos<DCH>(j >= NI, j < NI ? j : j - NI, lane, row, off);
+                const int g0 = tile_load_group<DCH>(j >= NI, j < NI ? j : j - NI);
+                const int pkey = tb + min(g0, last);
+                const int pg = __builtin_amdgcn_readfirstlane(page_cache[(pkey >> a.page_shift) - tpage0]);
+                const char *base = (j < NI ? kc_b : vc_b) + (uint64_t)pg * ppage;
+                const int key = tb + min(row, last);
+                load_lds_saddr(base, (uint32_t)(key & a.page_mask) * prow + off, sb + ld_lds(i));
+            }
+        }
+    };
+
+    // the first tiles go to stages 0 .. NS - SCR - 1 while the masks are built in the last SCR
+    // stages; tile k always lives in stage k % NS
+    int issued = 0;
+    for (; issued < min(n_mt, NS - SCR); ++issued) issue_masked(issued, issued);
+    {
+        AncestorLds &anc = *reinterpret_cast<AncestorLds *>(smem + (NS - SCR) * STAGE_B);
+        const int cur = build_ancestor_masks(a.parent + (int64_t)b * a.T, a.T, anc, a.err, tid, NT);
+        const int W = (a.T + 63) >> 6;
+        for (int e = tid; e < a.T * W; e += NT) node_mask[e / W][e % W] = anc.m[cur][e / W][e % W];
+    }
+    wait_vmem<0>();   // the prefetched tiles have landed
+    __syncthreads();  // masks and tiles visible; the scratch stages are free for the ring
+
+    const int node_of = r < R ? r / G : -1;
+    auto mask_masked = [&](f32x16 &S, int t, int jb) TA_INLINE {
+        if (t >= n_tail) {
+            const uint64_t word = node_of >= 0 ? node_mask[node_of][t - n_tail] : 0ull;
+            const uint32_t bits = (uint32_t)(word >> (jb * 32 + 4 * hf));
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (!((bits >> (8 * (q >> 2) + (q & 3))) & 1u)) S[q] = -INFINITY;
+        } else {
+            const int kb = tb + jb * 32;
+            if (kb + 32 > L) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    if (kb + 8 * (q >> 2) + 4 * hf + (q & 3) >= L) S[q] = -INFINITY;
+            }
+        }
+    };
+    auto exps_exact = [&](const f32x16 &S, bf16x8 (&P)[2]) TA_INLINE {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) mx = fmaxf(mx, S[q]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        if (__any(m_new > m_run)) {
+            const float alpha =
+                m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[dt][q] *= alpha;
+            m_run = m_new;
+        }
+        const float mb = m_run == -INFINITY ? 0.f : m_run * c2;
+        float sum = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pe_ = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * u + e], c2, -mb));
+                sum += pe_;
+                P[u][e] = (__bf16)pe_;
+            }
+        l_run += sum;
+    };
+
+    reset_acc();
+    m_run = -INFINITY;
+    for (int t = 0; t < n_mt; ++t) {
+        const int after = min(NS - 2, n_mt - 1 - t);
+        if (after >= 2) wait_vmem<2 * NIW>();
+        else if (after == 1) wait_vmem<NIW>();
+        else wait_vmem<0>();
+        lds_barrier();
+        for (; issued < min(n_mt, t + NS); ++issued) issue_masked(issued, issued % NS);
+        if (!wave_active) continue;
+        const char *Ks = smem + (t % NS) * STAGE_B;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            f32x16 S;
+            bf16x8 P[2], vf[2][DT];
+            qk(Ks, jb, S);
+            load_vt(Ks + TILE_B, jb, vf);
+            mask_masked(S, t, jb);
+            exps_exact(S, P);
+            pv(vf, P);
+        }
+    }
+    write_part(a.n_splits);
 }
 
 hipError_t launch_attn_prefix(const AttnArgs &a, int nw, hipStream_t s) {

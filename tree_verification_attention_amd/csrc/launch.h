@@ -15,8 +15,10 @@ constexpr int kPageCache = 2048;
 
 // Device-side view of one attention launch. Part p (0 <= p < n_splits) covers prefix keys
 // [p * chunk, min((p + 1) * chunk, seq_len)) when with_prefix is set (the bf16 prefix kernel
-// stops at the last multiple of kKeyTile of seq_len), and the last part also covers the masked
-// tree keys when with_tree is set. With tail_only (masked kernel, one part) the prefix keys are
+// stops at the last multiple of kKeyTile of seq_len). With with_tree, the masked part (the tree
+// keys; for the bf16 prefix kernel also the prefix keys past its last full tile) is computed by
+// the last part's workgroups: the bf16 prefix kernel writes it to part n_splits, the fp32 kernel
+// folds it into its last part. With tail_only (masked kernel, one part) the prefix keys are
 // [seq_len rounded down to kKeyTile, seq_len) instead. Partial outputs go to
 // out_o[part][row][D] and out_lse[part][row], row = (b * T + node) * Hq + head.
 struct AttnArgs {
