@@ -112,6 +112,7 @@ SMALL = [
     ("g5_two_rowblocks", wl(B=1, Hq=10, Hkv=2, T=128, L=(60, 200), depth_cap=12), {}),
     ("g4_t128_rowblocks", wl(B=2, Hq=8, Hkv=2, T=128, L=(1, 130)), {}),
     ("chain_t256", wl(B=1, Hq=2, Hkv=1, T=256, L=70, tree="chain"), {}),
+    ("d64_t200_masked_ring", wl(B=2, Hq=4, Hkv=2, D=64, T=200, L=(65, 300), depth_cap=30), {}),
     ("single_node", wl(B=3, T=1, tree="single", L=(0, 129)), {}),
     ("star", wl(B=2, T=20, tree="star", L=(64, 64)), {}),
     ("uniform_f32_d128", wl(D=128, T=9, dtype="f32", tree="uniform", L=(1, 300)), {}),
@@ -163,7 +164,7 @@ def test_fused_tree_part_matches_tree_call(layout):
     workgroups go on with it). With prefix lengths of whole 64-key tiles there is no tail, so
     that part must equal what tree_attn_tree returns, bit for bit: the same per-row arithmetic
     over the same tree tiles. Several row blocks, D = 64 and 128."""
-    for D, T, Hq, Hkv in ((128, 64, 8, 2), (64, 40, 4, 4), (128, 100, 10, 2)):
+    for D, T, Hq, Hkv in ((128, 64, 8, 2), (64, 40, 4, 4), (128, 100, 10, 2), (64, 200, 4, 2)):
         w = wl(B=3, Hq=Hq, Hkv=Hkv, D=D, T=T, L=(130, 900))
         case = inputs.make_case(w, 5, layout=layout, page_size=16 if D == 64 else 64)
         case.seq_lens[:] = (case.seq_lens // 64) * 64
