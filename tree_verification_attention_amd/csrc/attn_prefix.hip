@@ -123,6 +123,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
     const uint32_t prow = 2u * (uint32_t)a.kv_s1;
     const uint64_t ppage = 2ull * (uint64_t)a.kv_s0;
     uint32_t ld_voff[NIW];
+    int ld_group[NIW];      // paged: first key (in the tile) of the instruction's aligned group
+    int64_t ld_pofs[NIW];   // paged, pages below 64 keys: byte offset of the group's page start
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
         const int j = wave * NIW + i;
@@ -130,6 +132,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
         uint32_t off;
         tile_load_pos<DCH>(j >= NI, j < NI ? j : j - NI, lane, row, off);
         ld_voff[i] = (uint32_t)row * prow + off;
+        ld_group[i] = tile_load_group<DCH>(j >= NI, j < NI ? j : j - NI);
+        ld_pofs[i] = PAGED ? (int64_t)((ld_group[i] & a.page_mask) - ld_group[i]) * prow : 0;
     }
     auto ld_lds = [&](int i) TA_INLINE -> uint32_t {  // LDS offset of the instruction's 1 KB
         const int j = wave * NIW + i;
@@ -153,15 +157,28 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < NIW; ++i)
                 load_lds_saddr(wave * NIW + i < NI ? kb : vb, ld_voff[i], st + ld_lds(i));
+        } else if (a.page_shift >= 6) {
+            // pages of 64 keys or more hold whole tiles: one block-table entry per tile
+            const int pg = __builtin_amdgcn_readfirstlane(page_cache[(k0 >> a.page_shift) - page0]);
+            const uint64_t off =
+                (uint64_t)(uint32_t)pg * ppage + (uint64_t)(uint32_t)(k0 & a.page_mask) * prow;
+            const char *kb = kc_b + off;
+            const char *vb = vc_b + off;
+#pragma unroll
+            for (int i = 0; i < NIW; ++i)
+                load_lds_saddr(wave * NIW + i < NI ? kb : vb, ld_voff[i], st + ld_lds(i));
         } else {
+            // 16- or 32-key pages: one entry per instruction, all read before the first load; the
+            // tile starts a page, so an instruction's rows sit at a fixed offset in theirs
+            int pgs[NIW];
+#pragma unroll
+            for (int i = 0; i < NIW; ++i)
+                pgs[i] = page_cache[((k0 + ld_group[i]) >> a.page_shift) - page0];
 #pragma unroll
             for (int i = 0; i < NIW; ++i) {
-                const int j = wave * NIW + i;
-                const int g0 = tile_load_group<DCH>(j >= NI, j < NI ? j : j - NI);
-                const int key = k0 + g0;
-                const int pg = __builtin_amdgcn_readfirstlane(page_cache[(key >> a.page_shift) - page0]);
-                const char *base = (j < NI ? kc_b : vc_b) + (uint64_t)pg * ppage +
-                                   (int64_t)((key & a.page_mask) - g0) * prow;
+                const int pg = __builtin_amdgcn_readfirstlane(pgs[i]);
+                const char *base = (wave * NIW + i < NI ? kc_b : vc_b) +
+                                   (uint64_t)(uint32_t)pg * ppage + ld_pofs[i];
                 load_lds_saddr(base, ld_voff[i], st + ld_lds(i));
             }
         }
