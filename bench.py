@@ -750,6 +750,17 @@ def main():
                              "kernel_avg_us": round(statistics.mean(r2["kernel_us"]), 2)}
         del case2
         torch.cuda.empty_cache()
+        # the same layer with its prefix in a page pool (64-key pages in random order)
+        case3 = inputs.make_case(wl, args.seed, layout="paged", page_size=64, pad="finite")
+        r3 = time_case(case3, args.steps, args.warmup, "gqa_64k_pinned paged")
+        ms3 = r3["wall_s"] * 1e3 / args.steps
+        line["paged"] = {"workload": "the headline layer, prefix in a pool of 64-key pages "
+                                     "(random page order, block table per sequence)",
+                         "us_per_layer": round(ms3 * 1e3, 2),
+                         "tb_per_s": round(work["step_bytes"] / (ms3 * 1e-3) / 1e12, 4),
+                         "kernel_avg_us": round(statistics.mean(r3["kernel_us"]), 2)}
+        del case3
+        torch.cuda.empty_cache()
     if not args.no_next_rows and wl.name == "gqa_64k_pinned":
         line["next_rows"] = time_next_rows(args.steps, args.warmup, args.seed)
         torch.cuda.empty_cache()
