@@ -74,7 +74,9 @@ typedef enum ta_dtype {
  *   v_cache    with strides (kv_s0 = batch, kv_s1 = row, kv_s2 = head). Paged layout: a page
  *              pool [num_pages, page_size, Hkv, D] with strides (kv_s0 = page, kv_s1 = row,
  *              kv_s2 = head); key j of sequence b lives in page block_table[b][j / page_size]
- *              at row j % page_size. K and V share one stride set.
+ *              at row j % page_size. K and V share one stride set. Strides are elements, each
+ *              a multiple of 16 bytes; 64 rows (contiguous) or one page (paged) must span less
+ *              than 2^31 bytes, the whole cache may be larger.
  *   seq_lens   int32 [B]: prefix length of each sequence, 0 <= seq_lens[b] <= capacity, where
  *              capacity = Lmax (contiguous) or max_blocks * page_size (paged).
  *   block_table int32 [B, max_blocks] or NULL. page_size is a power of two >= 16.

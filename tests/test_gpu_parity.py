@@ -145,6 +145,31 @@ def test_forward_paged_page_sizes(psz):
     check(case, o, lse, o_ref, lse_ref, f"paged/{psz}")
 
 
+def test_forward_cache_rows_far_apart():
+    """A contiguous cache whose key rows are 2 MiB apart: the prefix spans more than 2^31 bytes,
+    so every tile is addressed from a 64-bit base (only offsets inside a 64-row tile are 32-bit)."""
+    w = wl(B=1, Hq=8, Hkv=1, D=128, T=16, L=1100)
+    case = inputs.make_case(w, 6)
+    g = to_gpu(case)
+    Lc = case.k_cache.shape[1]
+    row = 1 << 20   # elements between consecutive key rows
+    views = []
+    for name in ("k_cache", "v_cache"):
+        big = torch.empty(Lc * row, dtype=torch.bfloat16, device="cuda")
+        v = big.as_strided((1, Lc, 1, 128), (Lc * row, row, 128, 1))
+        v.copy_(g[name])
+        views.append((big, v))
+    say(f"far rows: {Lc} rows x {row * 2} bytes = {Lc * row * 2 / 2**30:.2f} GiB per tensor")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, lse = _lib.forward(g["q"], views[0][1], views[1][1], g["seq_lens"], g["k_tree"],
+                            g["v_tree"], g["parent"], scale=case.scale, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    o_ref, lse_ref = oracle.attend_case(case)
+    check(case, out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "far rows")
+    del views
+
+
 def test_unfused_calls_and_merge():
     w = wl(B=2, Hq=8, Hkv=2, D=128, T=24, L=(0, 500), tree="uniform")
     case = inputs.make_case(w, 3)

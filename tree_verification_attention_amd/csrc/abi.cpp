@@ -77,9 +77,9 @@ int check_prefix(const ta_problem *p) {
     }
     if (!p->k_cache || !p->v_cache || !aligned16(p->k_cache) || !aligned16(p->v_cache))
         return TA_EINVAL;
-    // the kernels address a sequence's rows with 32-bit byte offsets from a per-(sequence, head)
-    // base
-    const int64_t rows = p->block_table ? p->page_size : p->Lmax;
+    // the kernels address rows with 32-bit byte offsets from a 64-bit base per 64-key tile
+    // (contiguous) or per page (paged)
+    const int64_t rows = p->block_table ? p->page_size : ta::kKeyTile;
     if ((rows * p->kv_s1 + p->D) * es > INT32_MAX) return TA_EINVAL;
     if (p->block_table && p->kv_s0 > INT32_MAX) return TA_EINVAL;
     return TA_OK;
