@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libtreeattn.so")
-SOURCES = ["abi.cpp", "attn_prefix.hip", "attn_tree.hip", "attn_f32.hip", "mask_merge.hip", "accept.hip",
+SOURCES = ["abi.cpp", "attn_prefix.hip", "attn_f32.hip", "mask_merge.hip", "accept.hip",
            "spec.hip", "gdn.hip"]
 ARCH = "gfx950"
 

@@ -190,37 +190,42 @@ AttnArgs make_args(const ta_problem *p, const Plan &pl, int32_t *err) {
 
 int status(hipError_t e) { return e == hipSuccess ? TA_OK : TA_EHIP; }
 
-// The prefix splits into parts 0 .. n_splits - 1 of (wo, wl) (bf16: full 64-key tiles only).
-// With ``tree`` (bf16 only), the last split's workgroups go on with the masked part -- the prefix
-// keys past the last full tile and the tree keys -- into part n_splits, in the same launch.
+// The prefix splits into parts 0 .. n_splits - 1 of (wo, wl). bf16: the splits take the full
+// 64-key tiles, and the last split's workgroups go on, in the same launch, with the masked part
+// into part n_splits -- the prefix keys past the last full tile and, with ``tree``, the tree keys.
+// fp32: the splits take every prefix key; the tree is a launch of its own (launch_tree_part).
 int launch_prefix_parts(const ta_problem *p, const Plan &pl, int32_t *err, float *wo, float *wl,
                         bool tree, hipStream_t s) {
     AttnArgs a = make_args(p, pl, err);
     a.n_splits = pl.n_splits;
     a.with_prefix = 1;
-    a.with_tree = tree && p->dtype == TA_BF16;
     a.out_o = wo;
     a.out_lse = wl;
     a.part_so = pl.rows * p->D;
     a.part_sl = pl.rows;
-    return status(p->dtype == TA_BF16 ? ta::launch_attn_prefix(a, pl.nw, s) : ta::launch_attn_f32(a, s));
+    if (p->dtype != TA_BF16) return status(ta::launch_attn_f32(a, s));
+    a.with_tree = tree;
+    a.out_o_m = wo + pl.n_splits * a.part_so;
+    a.out_lse_m = wl + pl.n_splits * a.part_sl;
+    return status(ta::launch_attn_prefix(a, pl.nw, s));
 }
 
-// One masked part into (o, l): the tree keys when ``tree`` is set, and on the bf16 path the
-// prefix keys past the last full 64-key tile when ``tail`` is set.
-int launch_last_part(const ta_problem *p, const Plan &pl, int32_t *err, float *o, float *l,
-                     bool tail, bool tree, hipStream_t s) {
+// The masked tree part alone into (o, l): the bf16 prefix kernel with no prefix (its one split's
+// workgroups take only the masked part), or the fp32 kernel over the tree keys.
+int launch_tree_part(const ta_problem *p, const Plan &pl, int32_t *err, float *o, float *l,
+                     hipStream_t s) {
     AttnArgs a = make_args(p, pl, err);
-    // small work: 64 rows per workgroup (two wavefronts) spreads it over more compute units
-    const int R = p->T * (p->Hq / p->Hkv);
-    a.n_rb = (R + 63) / 64;
     a.n_splits = 1;
-    a.with_prefix = tail && p->dtype == TA_BF16;
-    a.tail_only = 1;
-    a.with_tree = tree;
-    a.out_o = o;
-    a.out_lse = l;
-    return status(p->dtype == TA_BF16 ? ta::launch_attn_tree(a, 2, s) : ta::launch_attn_f32(a, s));
+    a.with_prefix = 0;
+    a.with_tree = 1;
+    if (p->dtype != TA_BF16) {
+        a.out_o = o;
+        a.out_lse = l;
+        return status(ta::launch_attn_f32(a, s));
+    }
+    a.out_o_m = o;
+    a.out_lse_m = l;
+    return status(ta::launch_attn_prefix(a, pl.nw, s));
 }
 
 }  // namespace
@@ -277,14 +282,8 @@ int tree_attn_prefix(const ta_problem *p, float *o_c, float *lse_c, void *ws, si
     float *wo = static_cast<float *>(ws);
     float *wl = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
     if ((rc = launch_prefix_parts(p, pl, err_flag, wo, wl, false, stream))) return rc;
-    int parts = pl.n_splits;
-    if (p->dtype == TA_BF16) {
-        // the prefix keys past the last full tile, as one more part
-        if ((rc = launch_last_part(p, pl, err_flag, wo + pl.n_splits * pl.rows * p->D,
-                                   wl + pl.n_splits * pl.rows, true, false, stream)))
-            return rc;
-        parts += 1;
-    }
+    // bf16: the prefix keys past the last full tile are one more part
+    const int parts = pl.n_splits + (p->dtype == TA_BF16 ? 1 : 0);
     MergeArgs m{wo, wl, pl.rows * p->D, pl.rows, parts, nullptr, nullptr, pl.rows, p->D, o_c, lse_c};
     return status(ta::launch_merge(m, false, stream));
 }
@@ -297,7 +296,7 @@ int tree_attn_tree(const ta_problem *p, float *o_s, float *lse_s, int32_t *err_f
     if ((rc = check_tree(p))) return rc;
     if (!o_s || !lse_s) return TA_EINVAL;
     const Plan pl = make_plan(p);
-    return launch_last_part(p, pl, err_flag, o_s, lse_s, false, true, stream);
+    return launch_tree_part(p, pl, err_flag, o_s, lse_s, stream);
 }
 
 int tree_attn_merge(int B, int T, int Hq, int D, const float *o_a, const float *lse_a,
@@ -334,8 +333,8 @@ int tree_attn_partials(const ta_problem *p, void *ws, size_t ws_bytes, int32_t *
     float *wl = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
     if ((rc = launch_prefix_parts(p, pl, err_flag, wo, wl, true, stream))) return rc;
     if (p->dtype == TA_BF16) return TA_OK;  // the masked part rode with the last split
-    return launch_last_part(p, pl, err_flag, wo + pl.n_splits * pl.rows * p->D,
-                            wl + pl.n_splits * pl.rows, true, true, stream);
+    return launch_tree_part(p, pl, err_flag, wo + pl.n_splits * pl.rows * p->D,
+                            wl + pl.n_splits * pl.rows, stream);
 }
 
 int tree_attn_combine(const ta_problem *p, const void *ws, size_t ws_bytes, void *o, float *lse,

@@ -4,12 +4,11 @@
 // the whole committed prefix of its sequence (LongSpec page, "Fast tree attention"). This kernel
 // computes it over the prefix's full 64-key tiles, split along the prefix so that every compute
 // unit streams its own slice. The keys past the last full tile (fewer than 64) and the tree's
-// own keys form the masked part: when the tree rides along (tree_attn_partials / forward), the
-// last split's workgroups -- sized a few tiles short for it -- take it after their prefix tiles,
-// under the ancestor-or-self mask built in LDS; otherwise the masked tree kernel does. All parts
-// are combined afterwards by the log-sum-exp identity of the same section (merge kernel). The
-// prefix loop itself holds no mask, no ragged tile and no tree: nothing but the streaming and
-// the two products.
+// own keys form the masked part, which the last split's workgroups -- sized a few tiles short for
+// it -- take after their prefix tiles, under the ancestor-or-self mask built in LDS (the tree
+// alone, for tree_attn_tree, is the same part with no prefix). All parts are combined afterwards
+// by the log-sum-exp identity of the same section (merge kernel). The prefix loop itself holds
+// no mask, no ragged tile and no tree: nothing but the streaming and the two products.
 //
 // One workgroup handles one (part, kv-head, row block, sequence). Query packing: the G = Hq / Hkv
 // query heads sharing a KV head and the T tree nodes form R = T * G rows, row = node * G + group
@@ -74,7 +73,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
     const bool wave_active = row0 < R;
 
     // ---- this part's full tiles: [pb, pe), pe at most the last multiple of 64 of the length
-    int L = a.seq_lens[b];
+    int L = a.with_prefix ? a.seq_lens[b] : 0;
     if (L < 0 || L > a.capacity) {
         if (a.err && tid == 0) atomicOr(a.err, (int32_t)TA_DEV_BAD_LEN);
         L = L < 0 ? 0 : a.capacity;
@@ -338,13 +337,13 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
     // ---- normalise and write a part's (O, LSE); register r of O^T tile dt holds
     // d = dt*32 + 8*(r/4) + 4*hf + r%4
     const int r = row0 + l32;
-    auto write_part = [&](int slot) TA_INLINE {
+    auto write_part = [&](float *out_o, float *out_lse) TA_INLINE {
         const float l_tot = l_run + __shfl_xor(l_run, 32);
         if (r < R) {
             const int node = r / G, h = g * G + r % G;
             const int64_t orow = ((int64_t)b * a.T + node) * a.Hq + h;
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            float *op = a.out_o + slot * a.part_so + orow * D + 4 * hf;
+            float *op = out_o + orow * D + 4 * hf;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -356,23 +355,21 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
                     v.w = acc[dt][4 * q4 + 3] * inv;
                     *reinterpret_cast<float4 *>(op + dt * 32 + 8 * q4) = v;
                 }
-            if (hf == 0)
-                a.out_lse[slot * a.part_sl + orow] =
-                    l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+            if (hf == 0) out_lse[orow] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
         }
     };
-    write_part(part);
+    if (a.with_prefix) write_part(a.out_o + part * a.part_so, a.out_lse + part * a.part_sl);
 
-    // ---- the masked part, when the tree rides with the prefix: the last split (the shortest,
-    // or empty for short sequences) goes on with the prefix keys past the last full tile and the
-    // tree's own keys under the ancestor-or-self mask (LongSpec page, "Fast tree attention"),
-    // into part n_splits. Every masked tile takes the exact path: the running maximum moves to
-    // cover each block and what is accumulated is rescaled.
-    if (!a.with_tree || part != a.n_splits - 1) return;
+    // ---- the masked part: the last split (the shortest, or empty for short sequences) goes on
+    // with the prefix keys past the last full tile and, with the tree, the tree's own keys under
+    // the ancestor-or-self mask (LongSpec page, "Fast tree attention"), into out_o_m / out_lse_m.
+    // Every masked tile takes the exact path: the running maximum moves to cover each block and
+    // what is accumulated is rescaled.
+    if (part != a.n_splits - 1 || !(a.with_prefix || a.with_tree)) return;
     __syncthreads();  // every wavefront is done with the ring
     const int tb = L & ~(KT - 1);  // the tail: prefix keys [tb, L)
     const int n_tail = L > tb ? 1 : 0;
-    const int n_mt = n_tail + (a.T + KT - 1) / KT;
+    const int n_mt = n_tail + (a.with_tree ? (a.T + KT - 1) / KT : 0);
     int tpage0 = 0;
     if (PAGED && n_tail) {
         tpage0 = tb >> a.page_shift;
@@ -445,7 +442,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
     // stages; tile k always lives in stage k % NS
     int issued = 0;
     for (; issued < min(n_mt, NS - SCR); ++issued) issue_masked(issued, issued);
-    {
+    if (a.with_tree) {
         AncestorLds &anc = *reinterpret_cast<AncestorLds *>(smem + (NS - SCR) * STAGE_B);
         const int cur = build_ancestor_masks(a.parent + (int64_t)b * a.T, a.T, anc, a.err, tid, NT);
         const int W = (a.T + 63) >> 6;
@@ -522,7 +519,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
             pv(vf, P);
         }
     }
-    write_part(a.n_splits);
+    write_part(a.out_o_m, a.out_lse_m);
 }
 
 hipError_t launch_attn_prefix(const AttnArgs &a, int nw, hipStream_t s) {

@@ -14,13 +14,13 @@ constexpr int kRowsPerWave = 32;
 constexpr int kPageCache = 2048;
 
 // Device-side view of one attention launch. Part p (0 <= p < n_splits) covers prefix keys
-// [p * chunk, min((p + 1) * chunk, seq_len)) when with_prefix is set (the bf16 prefix kernel
-// stops at the last multiple of kKeyTile of seq_len). With with_tree, the masked part (the tree
-// keys; for the bf16 prefix kernel also the prefix keys past its last full tile) is computed by
-// the last part's workgroups: the bf16 prefix kernel writes it to part n_splits, the fp32 kernel
-// folds it into its last part. With tail_only (masked kernel, one part) the prefix keys are
-// [seq_len rounded down to kKeyTile, seq_len) instead. Partial outputs go to
+// [p * chunk, min((p + 1) * chunk, seq_len)) when with_prefix is set; partial outputs go to
 // out_o[part][row][D] and out_lse[part][row], row = (b * T + node) * Hq + head.
+//   bf16 (prefix kernel): the parts take the prefix's full kKeyTile tiles only. The last part's
+//   workgroups then compute the masked part -- the prefix keys past the last full tile (with
+//   with_prefix) and the tree keys under the ancestor mask (with_tree) -- into out_o_m /
+//   out_lse_m. Without with_prefix nothing is written to out_o / out_lse.
+//   fp32: with_tree folds the tree keys into the last part.
 struct AttnArgs {
     const void *q;
     int64_t q_sb, q_st, q_sh;
@@ -36,7 +36,6 @@ struct AttnArgs {
     int32_t n_splits;
     int32_t with_prefix;
     int32_t with_tree;
-    int32_t tail_only;
     int32_t chunk;      // prefix keys per split (multiple of kKeyTile)
     int32_t n_rb;       // row blocks per (b, kv-head)
     float scale;        // logit scale
@@ -44,6 +43,8 @@ struct AttnArgs {
     float *out_o;
     float *out_lse;
     int64_t part_so, part_sl;  // part strides (elements) of out_o / out_lse
+    float *out_o_m;            // bf16: the masked part's [row][D] and [row]
+    float *out_lse_m;
     int32_t *err;
 };
 
@@ -77,7 +78,6 @@ struct CommitArgs {
 hipError_t launch_mask(const int32_t *parent, int B, int T, uint64_t *mask, int32_t *err,
                        hipStream_t s);
 hipError_t launch_attn_prefix(const AttnArgs &a, int nw, hipStream_t s);
-hipError_t launch_attn_tree(const AttnArgs &a, int nw, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &m, bool out_bf16, hipStream_t s);
 struct GdnArgs {
