@@ -225,7 +225,10 @@ int launch_tree_part(const ta_problem *p, const Plan &pl, int32_t *err, float *o
     }
     a.out_o_m = o;
     a.out_lse_m = l;
-    return status(ta::launch_attn_prefix(a, pl.nw, s));
+    // little work and no prefix: 64 rows per workgroup (two wavefronts) spread the mask builds
+    // and the latency over more compute units
+    a.n_rb = (p->T * (p->Hq / p->Hkv) + 63) / 64;
+    return status(ta::launch_attn_prefix(a, 2, s));
 }
 
 }  // namespace
