@@ -145,6 +145,25 @@ def test_forward_paged_page_sizes(psz):
     check(case, o, lse, o_ref, lse_ref, f"paged/{psz}")
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_forward_capacity_beyond_lengths(layout):
+    """A cache allocated three times longer than the longest prefix: the splits are sized from the
+    lengths on the device, all of them still cover the prefix exactly once."""
+    w = wl(B=3, Hq=8, Hkv=2, D=128, T=24, L=(300, 2000))
+    case = inputs.make_case(w, 8, layout=layout, page_size=32 if layout == "paged" else 64,
+                            lcap=6000)
+    g = to_gpu(case)
+    p = _lib.make_problem(g["q"], g["k_cache"], g["v_cache"], g["seq_lens"], g["k_tree"],
+                          g["v_tree"], g["parent"], block_table=g["block_table"],
+                          page_size=g["page_size"], scale=case.scale)
+    say(f"capacity 6000 {layout}: lens={case.seq_lens.tolist()} splits={_lib.num_splits(p)}")
+    for splits in (0, 5):
+        o, lse, err = run_forward(case, num_splits=splits)
+        assert err == 0
+        o_ref, lse_ref = oracle.attend_case(case)
+        check(case, o, lse, o_ref, lse_ref, f"capacity/{layout}/splits={splits}")
+
+
 def test_forward_cache_rows_far_apart():
     """A contiguous cache whose key rows are 2 MiB apart: the prefix spans more than 2^31 bytes,
     so every tile is addressed from a 64-bit base (only offsets inside a 64-row tile are 32-bit)."""

@@ -24,6 +24,7 @@ struct Plan {
     int n_rb = 1;      // row blocks per (b, kv-head)
     int n_splits = 1;  // prefix splits
     int chunk = ta::kKeyTile;
+    int reserve = 0;   // keys' worth of time the last split keeps for the masked part
     int capacity = 0;  // prefix rows addressable per sequence
     int64_t rows = 0;  // B * T * Hq
     size_t o_bytes = 0, lse_bytes = 0;  // workspace regions for n_splits + 1 parts
@@ -135,6 +136,7 @@ Plan make_plan(const ta_problem *p) {
     const int64_t reserve = p->dtype == TA_BF16 && p->num_splits == 0
                                 ? (int64_t)ta::kKeyTile * ((p->T + ta::kKeyTile - 1) / ta::kKeyTile + 2)
                                 : 0;
+    pl.reserve = (int)reserve;
     int64_t chunk = pl.capacity > 0 ? ((int64_t)pl.capacity + reserve + n - 1) / n : 1;
     chunk = (chunk + ta::kKeyTile - 1) / ta::kKeyTile * ta::kKeyTile;
     if (p->block_table && p->dtype == TA_BF16) {
@@ -181,6 +183,7 @@ AttnArgs make_args(const ta_problem *p, const Plan &pl, int32_t *err) {
     a.G = p->Hq / p->Hkv;
     a.D = p->D;
     a.chunk = pl.chunk;
+    a.reserve = pl.reserve;
     a.n_rb = pl.n_rb;
     a.scale = p->scale;
     a.scale_log2 = p->scale * 1.4426950408889634f;

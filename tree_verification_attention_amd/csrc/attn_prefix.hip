@@ -72,14 +72,34 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
     const int row0 = (rb * NW + wave) * 32;
     const bool wave_active = row0 < R;
 
-    // ---- this part's full tiles: [pb, pe), pe at most the last multiple of 64 of the length
+    // ---- this part's full tiles: [pb, pe), pe at most the last multiple of 64 of the length.
+    // With several splits the chunk follows the longest prefix of the batch (every workgroup
+    // reads all the lengths), not the cache capacity, so a cache allocated longer than what it
+    // holds leaves no split idle; the host's chunk, sized from the capacity, bounds it (which
+    // keeps a paged part's block-table entries within the LDS cache).
+    __shared__ int len_max[NW];
     int L = a.with_prefix ? a.seq_lens[b] : 0;
     if (L < 0 || L > a.capacity) {
         if (a.err && tid == 0) atomicOr(a.err, (int32_t)TA_DEV_BAD_LEN);
         L = L < 0 ? 0 : a.capacity;
     }
-    const int pb = part * a.chunk;
-    const int pe = min(pb + a.chunk, L & ~(KT - 1));
+    int chunk = a.chunk;
+    if (a.with_prefix && a.n_splits > 1) {
+        int mx = 0;
+        for (int i = tid; i < a.B; i += NT) mx = max(mx, min(max(a.seq_lens[i], 0), a.capacity));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+        if (lane == 0) len_max[wave] = mx;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) mx = max(mx, len_max[w]);
+        const int64_t c = ((int64_t)mx + a.reserve + a.n_splits - 1) / a.n_splits;
+        // the same in every lane: keep it scalar, as the loop bounds below must be
+        chunk = __builtin_amdgcn_readfirstlane(
+            (int)min((int64_t)chunk, max((int64_t)KT, (c + KT - 1) & ~(int64_t)(KT - 1))));
+    }
+    const int pb = part * chunk;
+    const int pe = min(pb + chunk, L & ~(KT - 1));
     const int n_tiles = pe > pb ? (pe - pb) / KT : 0;
 
     // ---- paged layout: this part's block-table entries, validated, cached in LDS

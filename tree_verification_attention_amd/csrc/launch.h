@@ -36,7 +36,9 @@ struct AttnArgs {
     int32_t n_splits;
     int32_t with_prefix;
     int32_t with_tree;
-    int32_t chunk;      // prefix keys per split (multiple of kKeyTile)
+    int32_t chunk;      // prefix keys per split (multiple of kKeyTile); the bf16 kernel uses
+                        // at most this, sized on the device from the longest prefix
+    int32_t reserve;    // keys' worth of time the last split keeps for the masked part
     int32_t n_rb;       // row blocks per (b, kv-head)
     float scale;        // logit scale
     float scale_log2;   // scale * log2(e)
