@@ -119,13 +119,15 @@ int tree_mask_build(const int32_t *parent, int B, int T, uint64_t *mask, int32_t
                     hipStream_t stream);
 
 /*
- * Host-only. Bytes of workspace that tree_attn_prefix and tree_attn_forward need for ``p``
- * (one partial output and log-sum-exp per part, fp32; num_splits + 1 parts). Writes *bytes; returns TA_EINVAL /
- * TA_EUNSUPPORTED for a problem the other calls would reject.
+ * Host-only. Bytes of workspace that tree_attn_prefix, tree_attn_partials and tree_attn_forward
+ * need for ``p`` (2 S + 1 fp32 partial slots of O and LSE per row, S = tree_attn_num_splits(),
+ * and one int32 part count per sequence; layout at tree_attn_partials). Writes *bytes; returns
+ * TA_EINVAL / TA_EUNSUPPORTED for a problem the other calls would reject.
  */
 int tree_attn_workspace_size(const ta_problem *p, size_t *bytes);
 
-/* Host-only. The number of prefix splits the library uses for ``p`` (after automatic choice). */
+/* Host-only. The split count S the library plans for ``p`` (after automatic choice): every KV
+ * head's prefixes are cut into S * B parts, S per sequence on average. */
 int tree_attn_num_splits(const ta_problem *p, int *num_splits);
 
 /*
@@ -171,15 +173,18 @@ int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t
                       int32_t *err_flag, hipStream_t stream);
 
 /*
- * The divide step of tree_attn_forward on its own: every prefix split and the masked tree part
+ * The divide step of tree_attn_forward on its own: every prefix part and the masked tree part
  * write their partial (O, LSE) into ``ws`` (LongSpec page, "Fast tree attention", splitting the
- * key-value pairs; the prefix is further split along its length). Workspace layout, with
- * S = tree_attn_num_splits(), P = S + 1 parts and rows = B * T * Hq: fp32 O parts
- * [P][rows][D] at byte 0, then fp32 LSE parts [P][rows] at byte
- * tree_attn_workspace_lse_offset(). Part p < S covers one chunk of every sequence's prefix
- * (bf16: up to the last multiple of 64 of the sequence's length); part S covers the masked tree
- * keys and, for bf16, the prefix keys past that multiple of 64. An empty part has O = 0 and
- * LSE = -inf. A caller that shards the prefix over several devices exchanges these partials.
+ * key-value pairs; the prefix is further split along its length). With S =
+ * tree_attn_num_splits() and rows = B * T * Hq the workspace holds P = 2 S + 1 slots: fp32 O
+ * [P][rows][D] at byte 0, fp32 LSE [P][rows] at byte tree_attn_workspace_lse_offset(), then
+ * int32 counts [B] right after the LSE slots (at the lse offset plus P * rows * 4, rounded up to
+ * 256). Sequence b's prefix is split into counts[b] <= 2 S parts, in slots 0 .. counts[b] - 1 of
+ * its rows (the S * B parts of a KV head are dealt to the sequences by length, so a longer
+ * sequence gets more of them); bf16 parts hold whole 64-key tiles. Slot 2 S holds the masked
+ * tree keys and, for bf16, the prefix keys past the last multiple of 64. An empty part has
+ * O = 0 and LSE = -inf. A caller that shards the prefix over several devices exchanges these
+ * partials.
  */
 int tree_attn_partials(const ta_problem *p, void *ws, size_t ws_bytes, int32_t *err_flag,
                        hipStream_t stream);

@@ -27,8 +27,26 @@ struct Plan {
     int reserve = 0;   // keys' worth of time the last split keeps for the masked part
     int capacity = 0;  // prefix rows addressable per sequence
     int64_t rows = 0;  // B * T * Hq
-    size_t o_bytes = 0, lse_bytes = 0;  // workspace regions for n_splits + 1 parts
+    int slots = 2;     // partial slots per row: 2 n_splits prefix parts, then the masked part
+    size_t o_bytes = 0, lse_bytes = 0, cnt_bytes = 0;  // workspace regions
 };
+
+// The workspace of one problem: partial O [slots][rows][D], partial LSE [slots][rows], and the
+// prefix part count of every sequence [B].
+struct Workspace {
+    float *o, *lse;
+    int32_t *parts;
+};
+
+Workspace views(const Plan &pl, const void *ws) {
+    char *w = static_cast<char *>(const_cast<void *>(ws));
+    return Workspace{reinterpret_cast<float *>(w), reinterpret_cast<float *>(w + pl.o_bytes),
+                     reinterpret_cast<int32_t *>(w + pl.o_bytes + pl.lse_bytes)};
+}
+
+bool ws_ok(const Plan &pl, const void *ws, size_t ws_bytes) {
+    return ws && ((uintptr_t)ws & 255u) == 0 && ws_bytes >= pl.o_bytes + pl.lse_bytes + pl.cnt_bytes;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -146,9 +164,10 @@ Plan make_plan(const ta_problem *p) {
     }
     pl.chunk = (int)chunk;
     pl.n_splits = pl.capacity > 0 ? (int)((pl.capacity + chunk - 1) / chunk) : 1;
-    const int64_t parts = pl.n_splits + 1;
-    pl.o_bytes = align256((size_t)parts * pl.rows * p->D * sizeof(float));
-    pl.lse_bytes = align256((size_t)parts * pl.rows * sizeof(float));
+    pl.slots = 2 * pl.n_splits + 1;
+    pl.o_bytes = align256((size_t)pl.slots * pl.rows * p->D * sizeof(float));
+    pl.lse_bytes = align256((size_t)pl.slots * pl.rows * sizeof(float));
+    pl.cnt_bytes = align256((size_t)p->B * sizeof(int32_t));
     return pl;
 }
 
@@ -193,23 +212,25 @@ AttnArgs make_args(const ta_problem *p, const Plan &pl, int32_t *err) {
 
 int status(hipError_t e) { return e == hipSuccess ? TA_OK : TA_EHIP; }
 
-// The prefix splits into parts 0 .. n_splits - 1 of (wo, wl). bf16: the splits take the full
-// 64-key tiles, and the last split's workgroups go on, in the same launch, with the masked part
-// into part n_splits -- the prefix keys past the last full tile and, with ``tree``, the tree keys.
-// fp32: the splits take every prefix key; the tree is a launch of its own (launch_tree_part).
-int launch_prefix_parts(const ta_problem *p, const Plan &pl, int32_t *err, float *wo, float *wl,
+// The prefix parts of every sequence into the workspace slots, their counts into w.parts. bf16:
+// the parts take the full 64-key tiles, and each sequence's last part goes on, in the same
+// launch, with the masked part into the last slot -- the prefix keys past the last full tile
+// and, with ``tree``, the tree keys. fp32: n_splits parts of every prefix key; the tree is a
+// launch of its own (launch_tree_part).
+int launch_prefix_parts(const ta_problem *p, const Plan &pl, int32_t *err, const Workspace &w,
                         bool tree, hipStream_t s) {
     AttnArgs a = make_args(p, pl, err);
     a.n_splits = pl.n_splits;
     a.with_prefix = 1;
-    a.out_o = wo;
-    a.out_lse = wl;
+    a.out_o = w.o;
+    a.out_lse = w.lse;
     a.part_so = pl.rows * p->D;
     a.part_sl = pl.rows;
+    a.seq_parts = w.parts;
     if (p->dtype != TA_BF16) return status(ta::launch_attn_f32(a, s));
     a.with_tree = tree;
-    a.out_o_m = wo + pl.n_splits * a.part_so;
-    a.out_lse_m = wl + pl.n_splits * a.part_sl;
+    a.out_o_m = w.o + (int64_t)(pl.slots - 1) * a.part_so;
+    a.out_lse_m = w.lse + (int64_t)(pl.slots - 1) * a.part_sl;
     return status(ta::launch_attn_prefix(a, pl.nw, s));
 }
 
@@ -264,7 +285,7 @@ int tree_attn_workspace_size(const ta_problem *p, size_t *bytes) {
     int rc = check_shape(p);
     if (rc) return rc;
     const Plan pl = make_plan(p);
-    *bytes = pl.o_bytes + pl.lse_bytes;
+    *bytes = pl.o_bytes + pl.lse_bytes + pl.cnt_bytes;
     return TA_OK;
 }
 
@@ -284,13 +305,15 @@ int tree_attn_prefix(const ta_problem *p, float *o_c, float *lse_c, void *ws, si
     if ((rc = check_prefix(p))) return rc;
     if (!o_c || !lse_c) return TA_EINVAL;
     const Plan pl = make_plan(p);
-    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
-    float *wo = static_cast<float *>(ws);
-    float *wl = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
-    if ((rc = launch_prefix_parts(p, pl, err_flag, wo, wl, false, stream))) return rc;
-    // bf16: the prefix keys past the last full tile are one more part
-    const int parts = pl.n_splits + (p->dtype == TA_BF16 ? 1 : 0);
-    MergeArgs m{wo, wl, pl.rows * p->D, pl.rows, parts, nullptr, nullptr, pl.rows, p->D, o_c, lse_c};
+    if (!ws_ok(pl, ws, ws_bytes)) return TA_EWORKSPACE;
+    const Workspace w = views(pl, ws);
+    if ((rc = launch_prefix_parts(p, pl, err_flag, w, false, stream))) return rc;
+    // bf16: the prefix keys past the last full tile are one more part, in the last slot
+    const bool tail = p->dtype == TA_BF16;
+    const int64_t last = (int64_t)(pl.slots - 1) * pl.rows;
+    MergeArgs m{w.o, w.lse, pl.rows * p->D, pl.rows, pl.n_splits,
+                tail ? w.o + last * p->D : nullptr, tail ? w.lse + last : nullptr, pl.rows, p->D,
+                o_c, lse_c, w.parts, (int64_t)p->T * p->Hq};
     return status(ta::launch_merge(m, false, stream));
 }
 
@@ -334,13 +357,12 @@ int tree_attn_partials(const ta_problem *p, void *ws, size_t ws_bytes, int32_t *
     if (p->B == 0) return TA_OK;
     if ((rc = check_prefix(p)) || (rc = check_tree(p))) return rc;
     const Plan pl = make_plan(p);
-    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
-    float *wo = static_cast<float *>(ws);
-    float *wl = reinterpret_cast<float *>(static_cast<char *>(ws) + pl.o_bytes);
-    if ((rc = launch_prefix_parts(p, pl, err_flag, wo, wl, true, stream))) return rc;
-    if (p->dtype == TA_BF16) return TA_OK;  // the masked part rode with the last split
-    return launch_tree_part(p, pl, err_flag, wo + pl.n_splits * pl.rows * p->D,
-                            wl + pl.n_splits * pl.rows, stream);
+    if (!ws_ok(pl, ws, ws_bytes)) return TA_EWORKSPACE;
+    const Workspace w = views(pl, ws);
+    if ((rc = launch_prefix_parts(p, pl, err_flag, w, true, stream))) return rc;
+    if (p->dtype == TA_BF16) return TA_OK;  // the masked part rode with the last parts
+    const int64_t last = (int64_t)(pl.slots - 1) * pl.rows;
+    return launch_tree_part(p, pl, err_flag, w.o + last * p->D, w.lse + last, stream);
 }
 
 int tree_attn_combine(const ta_problem *p, const void *ws, size_t ws_bytes, void *o, float *lse,
@@ -350,11 +372,11 @@ int tree_attn_combine(const ta_problem *p, const void *ws, size_t ws_bytes, void
     if (p->B == 0) return TA_OK;
     if (!o || !lse) return TA_EINVAL;
     const Plan pl = make_plan(p);
-    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.o_bytes + pl.lse_bytes) return TA_EWORKSPACE;
-    const float *wo = static_cast<const float *>(ws);
-    const float *wl = reinterpret_cast<const float *>(static_cast<const char *>(ws) + pl.o_bytes);
-    MergeArgs m{wo, wl, pl.rows * p->D, pl.rows, pl.n_splits + 1, nullptr, nullptr,
-                pl.rows, p->D, o, lse};
+    if (!ws_ok(pl, ws, ws_bytes)) return TA_EWORKSPACE;
+    const Workspace w = views(pl, ws);
+    const int64_t last = (int64_t)(pl.slots - 1) * pl.rows;
+    MergeArgs m{w.o, w.lse, pl.rows * p->D, pl.rows, pl.n_splits, w.o + last * p->D, w.lse + last,
+                pl.rows, p->D, o, lse, w.parts, (int64_t)p->T * p->Hq};
     return status(ta::launch_merge(m, p->dtype == TA_BF16, stream));
 }
 

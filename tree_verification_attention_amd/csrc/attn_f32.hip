@@ -29,6 +29,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     const int b = (int)(row / ((int64_t)a.Hq * a.T));
     const int g = h / a.G;
     const bool has_tree = a.with_tree && part == a.n_splits - 1;
+    if (a.seq_parts && a.with_prefix && row == 0 && part == 0)
+        for (int i = lane; i < a.B; i += 64) a.seq_parts[i] = a.n_splits;
 
     const float *q = reinterpret_cast<const float *>(a.q) + b * a.q_sb + node * a.q_st + h * a.q_sh;
     for (int d = lane; d < D; d += 64) qs[d] = q[d];

@@ -41,6 +41,30 @@
 
 namespace ta {
 
+__device__ TA_INLINE int64_t wave_sum64(int64_t v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ TA_INLINE int64_t wave_max64(int64_t v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, (int64_t)__shfl_xor(v, o));
+    return v;
+}
+
+// exclusive prefix sum over the 64 lanes of a wavefront
+__device__ TA_INLINE int wave_exclusive_sum(int v) {
+    const int lane = threadIdx.x & 63;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    return x - v;
+}
+
 template <int D, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
     constexpr int KT = kKeyTile;
@@ -65,38 +89,95 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hf = lane >> 5, l32 = lane & 31;
-    const int part = blockIdx.x;
     const int g = blockIdx.y / a.n_rb, rb = blockIdx.y % a.n_rb;
-    const int b = blockIdx.z;
     const int G = a.G, R = a.T * G;
     const int row0 = (rb * NW + wave) * 32;
     const bool wave_active = row0 < R;
+    const bool first_wg = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0;
 
-    // ---- this part's full tiles: [pb, pe), pe at most the last multiple of 64 of the length.
-    // With several splits the chunk follows the longest prefix of the batch (every workgroup
-    // reads all the lengths), not the cache capacity, so a cache allocated longer than what it
-    // holds leaves no split idle; the host's chunk, sized from the capacity, bounds it (which
-    // keeps a paged part's block-table entries within the LDS cache).
+    // ---- which sequence, which of its parts, and the part's keys [pb, pe) (full tiles only).
+    // Without a prefix, or with one split: sequence blockIdx.z, part blockIdx.x. With several
+    // splits and at most 64 sequences the B * n_splits workgroups of this (kv head, row block)
+    // are dealt to the sequences by their work -- full prefix tiles plus the masked part's
+    // reserve -- so that a ragged batch is not paced by its longest sequence: every sequence
+    // first gets the parts its block-table entries need (paged) or one, the rest go out in
+    // proportion to the work, and leftovers one at a time to the sequence with the most work
+    // per part; a sequence gets at most 2 n_splits parts. With more sequences every one gets
+    // n_splits parts of a chunk sized from the longest prefix. Either way the cache capacity
+    // plays no part, so a cache allocated longer than what it holds leaves no split idle.
+    __shared__ int deal[5];  // sequence (-1: no part for this workgroup), part, chunk, length, parts
     __shared__ int len_max[NW];
-    int L = a.with_prefix ? a.seq_lens[b] : 0;
-    if (L < 0 || L > a.capacity) {
-        if (a.err && tid == 0) atomicOr(a.err, (int32_t)TA_DEV_BAD_LEN);
-        L = L < 0 ? 0 : a.capacity;
-    }
-    int chunk = a.chunk;
-    if (a.with_prefix && a.n_splits > 1) {
-        int mx = 0;
-        for (int i = tid; i < a.B; i += NT) mx = max(mx, min(max(a.seq_lens[i], 0), a.capacity));
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
-        if (lane == 0) len_max[wave] = mx;
+    int b = blockIdx.z, part = blockIdx.x, chunk = a.chunk, L = 0, n_parts = a.n_splits;
+    const bool several = a.with_prefix && a.n_splits > 1;
+    if (several && a.B <= 64) {
+        if (wave == 0) {
+            const bool on = lane < a.B;
+            int lb = on ? a.seq_lens[lane] : 0;
+            if (lb < 0 || lb > a.capacity) {
+                if (a.err) atomicOr(a.err, (int32_t)TA_DEV_BAD_LEN);
+                lb = lb < 0 ? 0 : a.capacity;
+            }
+            const int64_t full = lb & ~(KT - 1);
+            const int64_t work = on ? full + a.reserve : 0;
+            // paged: a part's block-table entries must fit the LDS cache, so no part spans more
+            // than `most` keys (the host's split count already covers any length with such parts)
+            const int64_t most =
+                PAGED ? (((int64_t)(kPageCache - 2) << a.page_shift) & ~(int64_t)(KT - 1)) : 0;
+            const int cap = 2 * a.n_splits;
+            int nb = on ? (PAGED ? (int)max((int64_t)1, (full + most - 1) / most) : 1) : 0;
+            const int64_t n_wg = (int64_t)a.n_splits * a.B;
+            const int64_t total = wave_sum64(work);
+            const int64_t rest = n_wg - wave_sum64(nb);
+            if (on && total > 0) nb = min(cap, nb + (int)(rest * work / total));
+            for (int it = 0; it < 8; ++it) {
+                if (wave_sum64(nb) >= n_wg) break;
+                // (work per part, lane) packed so that the maximum prefers the lower lane on ties
+                const int64_t key = on && nb < cap ? ((work / nb) << 8) | (63 - lane) : -1;
+                if (key == wave_max64(key) && key >= 0) ++nb;
+            }
+            int64_t cb = on ? ((work + nb - 1) / nb + KT - 1) & ~(int64_t)(KT - 1) : 0;
+            if (PAGED) cb = min(cb, most);
+            const int off = wave_exclusive_sum(nb);
+            const int wid = blockIdx.z * a.n_splits + blockIdx.x;
+            if (lane == 0) deal[0] = -1;
+            if (on && wid >= off && wid < off + nb) {
+                deal[0] = lane;
+                deal[1] = wid - off;
+                deal[2] = (int)min(cb, (int64_t)INT32_MAX);
+                deal[3] = lb;
+                deal[4] = nb;
+            }
+            if (first_wg && on && a.seq_parts) a.seq_parts[lane] = nb;
+        }
         __syncthreads();
+        b = __builtin_amdgcn_readfirstlane(deal[0]);
+        if (b < 0) return;  // more workgroups than parts: none for this one
+        part = __builtin_amdgcn_readfirstlane(deal[1]);
+        chunk = __builtin_amdgcn_readfirstlane(deal[2]);
+        L = __builtin_amdgcn_readfirstlane(deal[3]);
+        n_parts = __builtin_amdgcn_readfirstlane(deal[4]);
+    } else {
+        L = a.with_prefix ? a.seq_lens[b] : 0;
+        if (L < 0 || L > a.capacity) {
+            if (a.err && tid == 0) atomicOr(a.err, (int32_t)TA_DEV_BAD_LEN);
+            L = L < 0 ? 0 : a.capacity;
+        }
+        if (first_wg && a.with_prefix && a.seq_parts)
+            for (int i = tid; i < a.B; i += NT) a.seq_parts[i] = a.n_splits;
+        if (several) {
+            int mx = 0;
+            for (int i = tid; i < a.B; i += NT) mx = max(mx, min(max(a.seq_lens[i], 0), a.capacity));
 #pragma unroll
-        for (int w = 0; w < NW; ++w) mx = max(mx, len_max[w]);
-        const int64_t c = ((int64_t)mx + a.reserve + a.n_splits - 1) / a.n_splits;
-        // the same in every lane: keep it scalar, as the loop bounds below must be
-        chunk = __builtin_amdgcn_readfirstlane(
-            (int)min((int64_t)chunk, max((int64_t)KT, (c + KT - 1) & ~(int64_t)(KT - 1))));
+            for (int o = 32; o >= 1; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+            if (lane == 0) len_max[wave] = mx;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < NW; ++w) mx = max(mx, len_max[w]);
+            const int64_t c = ((int64_t)mx + a.reserve + a.n_splits - 1) / a.n_splits;
+            // the same in every lane: keep it scalar, as the loop bounds below must be
+            chunk = __builtin_amdgcn_readfirstlane(
+                (int)min((int64_t)chunk, max((int64_t)KT, (c + KT - 1) & ~(int64_t)(KT - 1))));
+        }
     }
     const int pb = part * chunk;
     const int pe = min(pb + chunk, L & ~(KT - 1));
@@ -385,7 +466,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
     // the ancestor-or-self mask (LongSpec page, "Fast tree attention"), into out_o_m / out_lse_m.
     // Every masked tile takes the exact path: the running maximum moves to cover each block and
     // what is accumulated is rescaled.
-    if (part != a.n_splits - 1 || !(a.with_prefix || a.with_tree)) return;
+    if (part != n_parts - 1 || !(a.with_prefix || a.with_tree)) return;
     __syncthreads();  // every wavefront is done with the ring
     const int tb = L & ~(KT - 1);  // the tail: prefix keys [tb, L)
     const int n_tail = L > tb ? 1 : 0;

@@ -13,14 +13,17 @@ constexpr int kRowsPerWave = 32;
 // Block-table entries of one part that the bf16 kernel caches in LDS (paged layout).
 constexpr int kPageCache = 2048;
 
-// Device-side view of one attention launch. Part p (0 <= p < n_splits) covers prefix keys
-// [p * chunk, min((p + 1) * chunk, seq_len)) when with_prefix is set; partial outputs go to
-// out_o[part][row][D] and out_lse[part][row], row = (b * T + node) * Hq + head.
-//   bf16 (prefix kernel): the parts take the prefix's full kKeyTile tiles only. The last part's
-//   workgroups then compute the masked part -- the prefix keys past the last full tile (with
-//   with_prefix) and the tree keys under the ancestor mask (with_tree) -- into out_o_m /
-//   out_lse_m. Without with_prefix nothing is written to out_o / out_lse.
-//   fp32: with_tree folds the tree keys into the last part.
+// Device-side view of one attention launch. With with_prefix, every sequence's prefix is
+// split into parts; part p of sequence b writes out_o[p][row][D] and out_lse[p][row], row =
+// (b * T + node) * Hq + head, and seq_parts[b] (when non-null) receives sequence b's part count.
+//   bf16 (prefix kernel): the B * n_splits workgroups of a (kv head, row block) are dealt to the
+//   sequences in proportion to their lengths (at most 2 n_splits parts each; see the kernel),
+//   and the parts take the prefix's full kKeyTile tiles only. Each sequence's last part then
+//   computes the masked part -- the prefix keys past the last full tile (with with_prefix) and
+//   the tree keys under the ancestor mask (with_tree) -- into out_o_m / out_lse_m. Without
+//   with_prefix nothing is written to out_o / out_lse.
+//   fp32: n_splits parts of chunk keys per sequence; with_tree folds the tree keys into the
+//   last part.
 struct AttnArgs {
     const void *q;
     int64_t q_sb, q_st, q_sh;
@@ -47,11 +50,13 @@ struct AttnArgs {
     int64_t part_so, part_sl;  // part strides (elements) of out_o / out_lse
     float *out_o_m;            // bf16: the masked part's [row][D] and [row]
     float *out_lse_m;
+    int32_t *seq_parts;        // [B] part count of every sequence, or null
     int32_t *err;
 };
 
 // Merge of n0 parts from (o0, lse0) (part strides so0 / sl0) plus, when o1 is non-null, one
-// more part (o1, lse1), into o (bf16 or fp32) and lse.
+// more part (o1, lse1), into o (bf16 or fp32) and lse. With seq_parts non-null, the rows of
+// sequence b = row / seq_rows take seq_parts[b] parts from (o0, lse0) instead of n0.
 struct MergeArgs {
     const float *o0, *lse0;
     int64_t so0, sl0;
@@ -61,6 +66,8 @@ struct MergeArgs {
     int32_t D;
     void *o;
     float *lse;
+    const int32_t *seq_parts;
+    int64_t seq_rows;
 };
 
 // Accepted-path KV commit: tree K/V rows path[b][j] (j < accept_len[b]) go to cache position

@@ -52,13 +52,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs m) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= m.rows) return;
-    const int n = m.n0 + (m.o1 ? 1 : 0);
+    const int n0 = m.seq_parts ? m.seq_parts[row / m.seq_rows] : m.n0;
+    const int n = n0 + (m.o1 ? 1 : 0);
 
     auto part_lse = [&](int p) -> float {
-        return p < m.n0 ? m.lse0[p * m.sl0 + row] : m.lse1[row];
+        return p < n0 ? m.lse0[p * m.sl0 + row] : m.lse1[row];
     };
     auto part_o = [&](int p) -> const float * {
-        return p < m.n0 ? m.o0 + p * m.so0 + row * D : m.o1 + row * D;
+        return p < n0 ? m.o0 + p * m.so0 + row * D : m.o1 + row * D;
     };
 
     float mx = -INFINITY;
