@@ -164,6 +164,21 @@ def test_forward_capacity_beyond_lengths(layout):
         check(case, o, lse, o_ref, lse_ref, f"capacity/{layout}/splits={splits}")
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_forward_very_ragged_batch(layout):
+    """Lengths 0, 70 and 40 000 in one batch: the parts are dealt by length (the long sequence
+    takes nearly all of them); with 16-key pages and two splits the long one needs two parts for
+    its block-table entries to fit the LDS cache."""
+    w = wl(B=3, Hq=4, Hkv=2, D=128, T=8, L=(0, 40000))
+    case = inputs.make_case(w, 9, layout=layout, page_size=16, lens=[0, 70, 40000])
+    for splits in (0, 2):
+        say(f"ragged {layout} splits={splits} lens={case.seq_lens.tolist()}")
+        o, lse, err = run_forward(case, num_splits=splits)
+        assert err == 0
+        o_ref, lse_ref = oracle.attend_case(case)
+        check(case, o, lse, o_ref, lse_ref, f"ragged/{layout}/splits={splits}")
+
+
 def test_forward_cache_rows_far_apart():
     """A contiguous cache whose key rows are 2 MiB apart: the prefix spans more than 2^31 bytes,
     so every tile is addressed from a 64-bit base (only offsets inside a 64-row tile are 32-bit)."""
