@@ -605,7 +605,7 @@ def stats_summary(stats_dir, workload, steps):
     lines = [
         f"# rocprofv3 kernel statistics, workload {workload}",
         f"# command: rocprofv3 --kernel-trace --stats -d STATS_DIR -o run --output-format csv -- "
-        f"python3 bench.py --workload {workload} --steps {steps} --warmup 5 --no-secondary "
+        f"python3 bench.py --workload {workload} --steps {steps} --warmup 10 --no-secondary "
         f"--no-cpu-baseline --no-next-rows",
         f"# summary: python3 bench.py --workload {workload} --steps {steps} --stats-summary STATS_DIR",
         "",
