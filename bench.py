@@ -605,7 +605,7 @@ def stats_summary(stats_dir, workload, steps):
     lines = [
         f"# rocprofv3 kernel statistics, workload {workload}",
         f"# command: rocprofv3 --kernel-trace --stats -d STATS_DIR -o run --output-format csv -- "
-        f"python3 bench.py --workload {workload} --steps {steps} --warmup 10 --no-secondary "
+        f"python3 bench.py --workload {workload} --steps {steps} --warmup 100 --no-secondary "
         f"--no-cpu-baseline --no-next-rows",
         f"# summary: python3 bench.py --workload {workload} --steps {steps} --stats-summary STATS_DIR",
         "",
@@ -633,7 +633,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="gqa_64k_pinned")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
