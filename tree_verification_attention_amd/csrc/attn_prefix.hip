@@ -89,14 +89,28 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hf = lane >> 5, l32 = lane & 31;
-    const int g = blockIdx.y / a.n_rb, rb = blockIdx.y % a.n_rb;
+    // XCD-aware order: consecutive workgroups go to the eight XCDs in turn (each with its own
+    // L2), so the logical order hands every XCD a contiguous range in which the row blocks of one
+    // (part, KV head, sequence) -- which stream the same K/V tiles -- are neighbours
+    int wg_x, wg_z, g, rb;
+    {
+        const int n = gridDim.x * gridDim.y * gridDim.z;
+        int w = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+        if ((n & 7) == 0) w = (w & 7) * (n >> 3) + (w >> 3);
+        rb = w % a.n_rb;
+        w /= a.n_rb;
+        wg_x = w % gridDim.x;
+        w /= gridDim.x;
+        g = w % a.Hkv;
+        wg_z = w / a.Hkv;
+    }
     const int G = a.G, R = a.T * G;
     const int row0 = (rb * NW + wave) * 32;
     const bool wave_active = row0 < R;
-    const bool first_wg = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0;
+    const bool first_wg = wg_x == 0 && g == 0 && rb == 0 && wg_z == 0;
 
     // ---- which sequence, which of its parts, and the part's keys [pb, pe) (full tiles only).
-    // Without a prefix, or with one split: sequence blockIdx.z, part blockIdx.x. With several
+    // Without a prefix, or with one split: sequence wg_z, part wg_x. With several
     // splits and at most 64 sequences the B * n_splits workgroups of this (kv head, row block)
     // are dealt to the sequences by their work -- full prefix tiles plus the masked part's
     // reserve -- so that a ragged batch is not paced by its longest sequence: every sequence
@@ -107,7 +121,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
     // plays no part, so a cache allocated longer than what it holds leaves no split idle.
     __shared__ int deal[5];  // sequence (-1: no part for this workgroup), part, chunk, length, parts
     __shared__ int len_max[NW];
-    int b = blockIdx.z, part = blockIdx.x, chunk = a.chunk, L = 0, n_parts = a.n_splits;
+    int b = wg_z, part = wg_x, chunk = a.chunk, L = 0, n_parts = a.n_splits;
     const bool several = a.with_prefix && a.n_splits > 1;
     if (several && a.B <= 64) {
         if (wave == 0) {
@@ -138,7 +152,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
             int64_t cb = on ? ((work + nb - 1) / nb + KT - 1) & ~(int64_t)(KT - 1) : 0;
             if (PAGED) cb = min(cb, most);
             const int off = wave_exclusive_sum(nb);
-            const int wid = blockIdx.z * a.n_splits + blockIdx.x;
+            const int wid = wg_z * a.n_splits + wg_x;
             if (lane == 0) deal[0] = -1;
             if (on && wid >= off && wid < off + nb) {
                 deal[0] = lane;
