@@ -90,13 +90,15 @@ __global__ __launch_bounds__(NW * 64) void attn_prefix_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hf = lane >> 5, l32 = lane & 31;
     // XCD-aware order: consecutive workgroups go to the eight XCDs in turn (each with its own
-    // L2), so the logical order hands every XCD a contiguous range in which the row blocks of one
-    // (part, KV head, sequence) -- which stream the same K/V tiles -- are neighbours
+    // L2). With several row blocks the logical order hands every XCD a contiguous range in which
+    // the row blocks of one (part, KV head, sequence) -- which stream the same K/V tiles -- are
+    // neighbours; with one row block the hardware order is kept (spreading every sequence over
+    // all XCDs streams faster there)
     int wg_x, wg_z, g, rb;
     {
         const int n = gridDim.x * gridDim.y * gridDim.z;
         int w = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-        if ((n & 7) == 0) w = (w & 7) * (n >> 3) + (w >> 3);
+        if (a.n_rb > 1 && (n & 7) == 0) w = (w & 7) * (n >> 3) + (w >> 3);
         rb = w % a.n_rb;
         w /= a.n_rb;
         wg_x = w % gridDim.x;
