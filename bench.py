@@ -162,7 +162,7 @@ def time_case(case, steps, warmup, label):
     flag = int(err.item())
     if flag:
         raise RuntimeError(f"device error flag {flag}")
-    print(f"[bench] {label}: done ({wall * 1e3 / steps:.1f} us/step wall)", file=sys.stderr,
+    print(f"[bench] {label}: done ({wall * 1e6 / steps:.1f} us/step wall)", file=sys.stderr,
           flush=True)
     return {"wall_s": wall, "step_us": step_us, "kernel_us": kern_us,
             "n_splits": _lib.num_splits(p), "ws_bytes": ws_bytes}
@@ -629,6 +629,38 @@ def stats_summary(stats_dir, workload, steps):
     print("\n".join(lines))
 
 
+def workload_table(steps, warmup, seed):
+    """One row per bf16 workload: fused forward (wall, back to back) and the split step (HIP
+    events after an evicting read), against the HBM and bf16 MFMA peaks."""
+    import gc
+
+    import torch
+
+    from tree_verification_attention_amd import inputs
+
+    print("| workload | B | T | Hq/Hkv | prefix | splits | forward us | TB/s | split step us | "
+          "frac HBM | TFLOP/s | frac MFMA |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for name, wl in inputs.WORKLOADS.items():
+        if wl.dtype != "bf16":
+            continue
+        case = inputs.make_case(wl, seed, pad="finite")
+        w = work_of(case)
+        r = time_case(case, steps, warmup, name)
+        fwd_us = r["wall_s"] * 1e6 / steps
+        k = statistics.mean(r["kernel_us"])
+        gbs = w["kernel_bytes"] / (k * 1e-6) / 1e9
+        tf = w["flops"] / (k * 1e-6) / 1e12
+        lens = case.seq_lens
+        pre = str(int(lens[0])) if lens.min() == lens.max() else f"{int(lens.min())}-{int(lens.max())}"
+        print(f"| {name} | {wl.B} | {wl.T} | {wl.Hq}/{wl.Hkv} | {pre} | {r['n_splits']} | "
+              f"{fwd_us:.1f} | {w['step_bytes'] / (fwd_us * 1e-6) / 1e12:.2f} | {k:.1f} | "
+              f"{gbs / HBM_PEAK_GBS:.3f} | {tf:.0f} | {tf / MFMA_BF16_PEAK_TFS:.3f} |", flush=True)
+        del case, r
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -652,6 +684,9 @@ def main():
                     help="summarise a rocprofv3 --stats run of --next-rows-only into profiles/")
     ap.add_argument("--stats-summary", metavar="STATS_DIR",
                     help="write the text summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--table", action="store_true",
+                    help="time every bf16 workload (fused forward and split step) and print a "
+                         "table row for each instead of the JSON line")
     args = ap.parse_args()
 
     if args.stats_summary:
@@ -685,6 +720,9 @@ def main():
 
     if args.next_rows_only:
         print(json.dumps(time_next_rows(args.steps, args.warmup, args.seed)), flush=True)
+        return
+    if args.table:
+        workload_table(args.steps, args.warmup, args.seed)
         return
     wl = inputs.WORKLOADS[args.workload]
     print(f"[bench] generating {wl.name} (seed {args.seed})", file=sys.stderr, flush=True)
