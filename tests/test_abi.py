@@ -80,6 +80,23 @@ def test_workspace_size_is_host_only_and_sane(lib):
     assert k2.value == 3
 
 
+def test_bf16_split_plan_fills_one_round_of_workgroups(lib):
+    """The planner's split count keeps the bf16 launch within one workgroup per CU (256 on a
+    host without a device, as on MI355X): 640 packed rows per KV head need three row blocks,
+    so 1 * 8 * 3 = 24 workgroups per split and 10 splits (11 would leave 8 waiting)."""
+    T, Hq, Hkv, L = 128, 40, 8, 131072
+    p = problem(B=1, T=T, Hq=Hq, Hkv=Hkv, Lmax=L, q_sb=T * Hq * 128, q_st=Hq * 128,
+                kv_s0=L * Hkv * 128, kv_s1=Hkv * 128, kt_sb=T * Hkv * 128, kt_st=Hkv * 128)
+    k = ctypes.c_int(0)
+    assert lib.tree_attn_num_splits(ctypes.byref(p), ctypes.byref(k)) == _lib.TA_OK
+    assert k.value == 10
+    # 32 workgroups per split divide the CUs exactly: 8 splits
+    p = problem(B=4, T=64, Hq=32, Hkv=8, Lmax=65536, q_sb=64 * 32 * 128, q_st=32 * 128,
+                kv_s0=65536 * 8 * 128, kv_s1=8 * 128, kt_sb=64 * 8 * 128, kt_st=8 * 128)
+    assert lib.tree_attn_num_splits(ctypes.byref(p), ctypes.byref(k)) == _lib.TA_OK
+    assert k.value == 8
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("D", 96, _lib.TA_EUNSUPPORTED), ("dtype", 7, _lib.TA_EUNSUPPORTED),
     ("T", 0, _lib.TA_EINVAL), ("T", 257, _lib.TA_EINVAL), ("Hq", 7, _lib.TA_EINVAL),

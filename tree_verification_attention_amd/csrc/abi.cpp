@@ -14,11 +14,13 @@ using ta::AttnArgs;
 using ta::MergeArgs;
 
 constexpr int kAbiVersion = 100;
-// Workgroups the prefix launch aims for per compute unit.
+// Workgroups the prefix launch aims for per compute unit (the bf16 kernel's 4-stage LDS ring of
+// K/V tiles leaves room for one workgroup per CU at D = 128).
 constexpr int kWgPerCu = 1;
 
-// Workspace parts: parts 0 .. n_splits - 1 hold the prefix splits; part n_splits holds the tree
-// keys and, on the bf16 path, the prefix keys past the last full 64-key tile.
+// Workspace slots per row: 2 n_splits for the prefix parts (a sequence gets at most that many
+// when the parts are dealt by length, n_splits otherwise), then the masked part (the tree keys
+// and the prefix keys past the last full 64-key tile) in the last slot.
 struct Plan {
     int nw = 1;        // wavefronts per workgroup (bf16 kernels)
     int n_rb = 1;      // row blocks per (b, kv-head)
@@ -142,7 +144,11 @@ Plan make_plan(const ta_problem *p) {
     int n = p->num_splits;
     if (n == 0) {
         const int64_t target = (int64_t)kWgPerCu * cu_count();
-        int64_t want = (target + wg_per_split - 1) / (wg_per_split > 0 ? wg_per_split : 1);
+        const int64_t per = wg_per_split > 0 ? wg_per_split : 1;
+        // bf16: round down, so that the launch never needs a second round of workgroups (with
+        // 24 workgroups per split, 10 splits take 368 us on the long-reasoning layer, 11 take
+        // 421 us: 8 workgroups wait for a free CU); fp32 workgroups are small, several share a CU
+        int64_t want = p->dtype == TA_BF16 ? target / per : (target + per - 1) / per;
         const int64_t most = (pl.capacity + 255) / 256;
         if (want > most) want = most;
         n = want < 1 ? 1 : (int)want;
