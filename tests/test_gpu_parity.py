@@ -118,6 +118,9 @@ SMALL = [
     ("uniform_f32_d128", wl(D=128, T=9, dtype="f32", tree="uniform", L=(1, 300)), {}),
     ("forced_splits_1", wl(L=(300, 700)), {"num_splits": 1}),
     ("forced_splits_7", wl(L=(300, 700)), {"num_splits": 7}),
+    # more than 64 sequences: every sequence takes S parts of a chunk sized from the longest
+    ("batch80_undealt", wl(B=80, Hq=2, Hkv=1, T=4, L=(0, 600)), {}),
+    ("batch70_forced_splits_3", wl(B=70, Hq=4, Hkv=2, T=8, L=(0, 400)), {"num_splits": 3}),
 ]
 
 
