@@ -135,10 +135,11 @@ def test_forward_small(name, w, kw):
         check(case, o, lse, o_ref, lse_ref, f"{name}/{layout}")
 
 
-@pytest.mark.parametrize("psz", [16, 32, 128, 256])
+@pytest.mark.parametrize("psz", [16, 32, 128, 256, 1024, 4096])
 def test_forward_paged_page_sizes(psz):
-    """Page sizes other than the small cases' 64 (D = 128): pages of 128 and 256 keys hold several
-    tiles (a tile can start mid-page), 16 and 32 split a tile over several pages."""
+    """Page sizes other than the small cases' 64 (D = 128): pages of 128 to 4096 keys hold several
+    tiles (a tile can start mid-page; at 4096 a whole sequence sits in one page), 16 and 32 split a
+    tile over several pages."""
     w = wl(B=3, Hq=8, Hkv=2, D=128, T=20, L=(1, 1500))
     case = inputs.make_case(w, 4, layout="paged", page_size=psz)
     say(f"paged page_size {psz} lens={case.seq_lens.tolist()}")
