@@ -93,44 +93,81 @@ def to_device(case):
                                                 "v_tree", "parent", "block_table")}
 
 
-def time_case(case, steps, warmup, label):
-    """Time ``steps`` fused forwards and ``steps`` dominant-kernel launches of ``case``."""
-    import ctypes
+class Launch:
+    """Device operands, outputs and workspace of one case, and its two timed calls: the fused
+    forward (tree_attn_forward) and the split step alone (tree_attn_partials)."""
 
+    def __init__(self, case):
+        import ctypes
+
+        import torch
+
+        from tree_verification_attention_amd import _lib
+
+        g = to_device(case)
+        self.g = g
+        self.p = _lib.make_problem(g["q"], g["k_cache"], g["v_cache"], g["seq_lens"], g["k_tree"],
+                                   g["v_tree"], g["parent"], block_table=g["block_table"],
+                                   page_size=case.page_size or None, scale=case.scale)
+        self.lib = _lib.load()
+        B, T, Hq, D = case.q.shape
+        self.out = torch.empty((B, T, Hq, D), dtype=g["q"].dtype, device="cuda")
+        self.lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
+        self.ws_bytes = _lib.workspace_size(self.p)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.stream = torch.cuda.current_stream()
+        sh = self.stream.cuda_stream
+        pp = ctypes.byref(self.p)
+        self.args_fwd = (pp, self.out.data_ptr(), self.lse.data_ptr(), self.ws.data_ptr(),
+                         self.ws_bytes, self.err.data_ptr(), sh)
+        self.args_part = (pp, self.ws.data_ptr(), self.ws_bytes, self.err.data_ptr(), sh)
+        self.n_splits = _lib.num_splits(self.p)
+        self._status = _lib.status_string
+
+    def fwd(self):
+        rc = self.lib.tree_attn_forward(*self.args_fwd)
+        if rc:
+            raise RuntimeError(f"tree_attn_forward: {self._status(rc)}")
+
+    def part(self):
+        rc = self.lib.tree_attn_partials(*self.args_part)
+        if rc:
+            raise RuntimeError(f"tree_attn_partials: {self._status(rc)}")
+
+    def check_flag(self):
+        flag = int(self.err.item())
+        if flag:
+            raise RuntimeError(f"device error flag {flag}")
+
+
+def events_around(fn, stream, steps, before=None):
+    """HIP events recorded on ``stream`` around each of ``steps`` calls of ``fn`` (``before``, if
+    given, runs ahead of each call outside the events); returns the durations in us."""
     import torch
 
-    from tree_verification_attention_amd import _lib
+    evs = []
+    for _ in range(steps):
+        if before is not None:
+            before()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]
 
-    g = to_device(case)
-    p = _lib.make_problem(g["q"], g["k_cache"], g["v_cache"], g["seq_lens"], g["k_tree"],
-                          g["v_tree"], g["parent"], block_table=g["block_table"],
-                          page_size=case.page_size or None, scale=case.scale)
-    lib = _lib.load()
-    B, T, Hq, D = case.q.shape
-    out = torch.empty((B, T, Hq, D), dtype=g["q"].dtype, device="cuda")
-    lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
-    ws_bytes = _lib.workspace_size(p)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-    pp = ctypes.byref(p)
-    args_fwd = (pp, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws_bytes, err.data_ptr(), sh)
-    args_part = (pp, ws.data_ptr(), ws_bytes, err.data_ptr(), sh)
 
-    def fwd():
-        rc = lib.tree_attn_forward(*args_fwd)
-        if rc:
-            raise RuntimeError(f"tree_attn_forward: {_lib.status_string(rc)}")
+def time_case(case, steps, warmup, label):
+    """Time ``steps`` fused forwards back to back and ``steps`` dominant-kernel launches of
+    ``case``, each of the latter after an evicting read."""
+    import torch
 
-    def part():
-        rc = lib.tree_attn_partials(*args_part)
-        if rc:
-            raise RuntimeError(f"tree_attn_partials: {_lib.status_string(rc)}")
-
+    L = Launch(case)
     print(f"[bench] {label}: warmup {warmup}", file=sys.stderr, flush=True)
     for _ in range(warmup):
-        fwd()
+        L.fwd()
     torch.cuda.synchronize()
     # timed region: exactly `steps` fused steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -138,9 +175,9 @@ def time_case(case, steps, warmup, label):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        ev[i][0].record(stream)
-        fwd()
-        ev[i][1].record(stream)
+        ev[i][0].record(L.stream)
+        L.fwd()
+        ev[i][1].record(L.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
@@ -148,24 +185,35 @@ def time_case(case, steps, warmup, label):
     # (outside the events) evicts the 256 MB last-level cache and the L2s
     evict = make_evict()
     for _ in range(warmup):
-        part()
+        L.part()
     torch.cuda.synchronize()
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(steps):
-        evict()
-        kev[i][0].record(stream)
-        part()
-        kev[i][1].record(stream)
-    torch.cuda.synchronize()
-    kern_us = [a.elapsed_time(b) * 1e3 for a, b in kev]
-    flag = int(err.item())
-    if flag:
-        raise RuntimeError(f"device error flag {flag}")
+    kern_us = events_around(L.part, L.stream, steps, evict)
+    L.check_flag()
     print(f"[bench] {label}: done ({wall * 1e6 / steps:.1f} us/step wall)", file=sys.stderr,
           flush=True)
     return {"wall_s": wall, "step_us": step_us, "kernel_us": kern_us,
-            "n_splits": _lib.num_splits(p), "ws_bytes": ws_bytes}
+            "n_splits": L.n_splits, "ws_bytes": L.ws_bytes}
+
+
+def time_evicted(case, steps, warmup, label):
+    """The fused forward and the split step of ``case``, each call timed with HIP events after a
+    512 MiB evicting read (every step starts from cold caches, as a layer of a decode step whose
+    KV was last touched one step earlier)."""
+    import torch
+
+    L = Launch(case)
+    evict = make_evict()
+    print(f"[bench] {label}: warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        L.fwd()
+    torch.cuda.synchronize()
+    fwd_us = events_around(L.fwd, L.stream, steps, evict)
+    for _ in range(warmup):
+        L.part()
+    torch.cuda.synchronize()
+    part_us = events_around(L.part, L.stream, steps, evict)
+    L.check_flag()
+    return {"fwd_us": fwd_us, "part_us": part_us, "n_splits": L.n_splits}
 
 
 def make_evict():
@@ -176,6 +224,114 @@ def make_evict():
     buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     out = torch.empty((), dtype=torch.float32, device="cuda")
     return lambda: torch.sum(buf, dim=0, out=out)
+
+
+# One entry per configuration the benchmark covers (the pages' workload families, all on seeded
+# synthetic inputs): (key, workload, layout, description).
+CONFIGS = [
+    ("tiny_f32", "tiny_f32", "contiguous",
+     "Tiny fp32: B=1, 4 q / 1 KV heads, D=64, prefix 256, 8-node tree (parent uniform in [-1, i-1])"),
+    ("mha_7b", "mha_7b", "contiguous",
+     "MHA 7B-layer bf16: B=1, 32/32 heads, D=128, prefix 16384, 64-node tree (depth<=8, <=4 children)"),
+    ("gqa_64k", "gqa_64k", "contiguous",
+     "GQA bf16: B=4, 32/8 heads, D=128, prefix lengths drawn in [32768, 65536], 64-node trees"),
+    ("gqa_64k_pinned", "gqa_64k_pinned", "contiguous",
+     "GQA bf16, every prefix 65536 (the headline layer), cold caches"),
+    ("gqa_64k_pinned_paged", "gqa_64k_pinned", "paged",
+     "the headline layer with its prefix in a pool of 64-key pages in random order"),
+    ("sweep_t1", "sweep_t1", "contiguous",
+     "tree-size sweep: B=8, 32/8 heads, D=128, prefix 32768, one node (plain decode)"),
+    ("sweep_t6", "sweep_t6", "contiguous", "tree-size sweep, 6-node chain"),
+    ("sweep_t16", "sweep_t16", "contiguous", "tree-size sweep, 16-node tree"),
+    ("sweep_t32", "sweep_t32", "contiguous", "tree-size sweep, 32-node tree"),
+    ("sweep_t64", "sweep_t64", "contiguous", "tree-size sweep, 64-node tree"),
+    ("sweep_t128", "sweep_t128", "contiguous", "tree-size sweep, 128-node tree"),
+    ("long_reasoning", "long_reasoning", "contiguous",
+     "Long-reasoning bf16: B=1, 40/8 heads, D=128, prefix 131072, 128-node tree (depth<=12), "
+     "K x8 on 4 channels"),
+    ("gqa_64k_beam", "gqa_64k_beam", "contiguous",
+     "GQA bf16 64k with a beam-search tree (layer widths 4, 16, 16, 16, 12)"),
+]
+
+
+def time_configs(steps, warmup, seed):
+    """Every configuration of CONFIGS: median / p10 / p90 of the fused forward and of the split
+    step (HIP events, evicting read before each call), bytes and flops against the HBM and bf16
+    MFMA peaks, and the node x q-head throughput."""
+    import gc
+
+    import torch
+
+    from tree_verification_attention_amd import inputs
+
+    out = {}
+    for key, name, layout, desc in CONFIGS:
+        wl = inputs.WORKLOADS[name]
+        case = inputs.make_case(wl, seed, layout=layout, page_size=64, pad="finite")
+        w = work_of(case)
+        r = time_evicted(case, steps, warmup, key)
+        f, k = statistics.median(r["fwd_us"]), statistics.median(r["part_us"])
+        lens = case.seq_lens
+        e = {"workload": desc, "B": wl.B, "T": wl.T, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D,
+             "dtype": wl.dtype, "prefix": [int(lens.min()), int(lens.max())],
+             "layout": layout, "splits": r["n_splits"],
+             "us_per_layer": round(f, 2), "us_p10": round(pct(r["fwd_us"], 0.1), 2),
+             "us_p90": round(pct(r["fwd_us"], 0.9), 2),
+             "split_step_us": round(k, 2),
+             "tb_per_s": round(w["step_bytes"] / (f * 1e-6) / 1e12, 4),
+             "frac_hbm": round(w["step_bytes"] / (f * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+             "split_frac_hbm": round(w["kernel_bytes"] / (k * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+             "node_qheads_per_s": round(wl.B * wl.T * wl.Hq / (f * 1e-6), 1),
+             "algorithmic_bytes": w["step_bytes"], "flops": w["flops"]}
+        if wl.dtype == "bf16":
+            e["tflops"] = round(w["flops"] / (f * 1e-6) / 1e12, 1)
+            e["frac_mfma"] = round(w["flops"] / (f * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+            e["split_frac_mfma"] = round(w["flops"] / (k * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+            e["bound"] = ("mfma" if w["flops"] / MFMA_BF16_PEAK_TFS > w["step_bytes"] / HBM_PEAK_GBS
+                          / 1e3 else "hbm")
+        else:
+            e["bound"] = "latency (fp32 path, 0.15 MB)"
+        out[key] = e
+        print(f"[bench] {key}: {f:.1f} us/layer (split {k:.1f} us), "
+              f"{e['tb_per_s']:.2f} TB/s", file=sys.stderr, flush=True)
+        del case, r
+        gc.collect()
+        torch.cuda.empty_cache()
+    return out
+
+
+def copy_ceiling(steps=10):
+    """A plain 1 GiB device-to-device copy (torch copy_, HIP events): 2 GiB of HBM traffic per
+    copy, the practical bandwidth ceiling to set beside the 8 TB/s peak."""
+    import torch
+
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    us = events_around(lambda: dst.copy_(src), torch.cuda.current_stream(), steps)
+    m = statistics.median(us)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_per_copy": 2 * COPY_BYTES, "us": round(m, 2),
+            "gbs": round(2 * COPY_BYTES / (m * 1e-6) / 1e9, 1),
+            "frac": round(2 * COPY_BYTES / (m * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "1 GiB read + 1 GiB written per copy, median of HIP-event timings"}
+
+
+def host_cpu():
+    """Host cores and CPU model for the CPU-baseline record."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "model": model}
 
 
 def time_breakdown(case, steps, warmup):
@@ -419,16 +575,6 @@ def traffic_entry(workload):
     return t
 
 
-def copy_calibration(n=5):
-    import torch
-    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    src.fill_(1)
-    for _ in range(n):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-
-
 UTIL_COUNTERS = ("MfmaUtil", "LdsBankConflict", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
                  "SQ_WAVES")
 
@@ -574,8 +720,11 @@ def accept_stats_summary(stats_dir, steps):
     print("\n".join(lines))
 
 
-def stats_summary(stats_dir, workload, steps):
-    """Text summary of a rocprofv3 --kernel-trace --stats run of this script."""
+def stats_summary(stats_dir, workload, steps, warmup):
+    """Text summary of a rocprofv3 --kernel-trace --stats run of this script's default JSON run:
+    the kernel statistics, then the headline layer's loops taken apart by position in the trace
+    (W warm-up forwards, the S timed forwards, W warm-up split steps, the S timed split steps, as
+    time_case issues them), with every forward step of the fresh process listed on its own."""
     import re
 
     def one(pattern):
@@ -588,26 +737,35 @@ def stats_summary(stats_dir, workload, steps):
         stats = list(csv.DictReader(f))
     with open(one("*kernel_trace.csv")) as f:
         trace = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
-    def durs_of(name):
-        return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-                for r in trace if name in r["Kernel_Name"]]
-    durs = durs_of(KERNEL_NAME)
-    alone = durs[-steps:]            # the kernel-alone loop: the last `steps` launches
-    fused = durs[:-steps][-steps:]   # the timed fused loop before it
-    bench_avg = None
+    spans = [(r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace]
+    prefix_idx = [i for i, (n, _, _) in enumerate(spans) if KERNEL_NAME in n]
+    W, S = warmup, steps
+    fwd_idx = prefix_idx[:W + S]                      # forwards: prefix kernel then merge kernel
+    fused = [(spans[i][2] - spans[i][1]) / 1e3 for i in prefix_idx[W:W + S]]
+    alone = [(spans[i][2] - spans[i][1]) / 1e3 for i in prefix_idx[2 * W + S:2 * W + 2 * S]]
+    step_rows = []
+    for k, i in enumerate(fwd_idx):
+        j = i + 1                                     # the combine launch follows on the stream
+        merge_us = (spans[j][2] - spans[j][1]) / 1e3 if "merge_kernel" in spans[j][0] else None
+        nxt = fwd_idx[k + 1] if k + 1 < len(fwd_idx) else None
+        step_us = (spans[nxt][1] - spans[i][1]) / 1e3 if nxt is not None else None
+        step_rows.append((k, (spans[i][2] - spans[i][1]) / 1e3, merge_us, step_us))
+    bench = {}
     logs = glob.glob(os.path.join(os.path.dirname(stats_dir.rstrip("/")),
                                   os.path.basename(stats_dir.rstrip("/")) + ".log"))
     if logs:
-        m = re.search(r'"kernel_avg_us": ([0-9.]+)', open(logs[0]).read())
-        bench_avg = float(m.group(1)) if m else None
+        txt = open(logs[0]).read()
+        for key in ("kernel_avg_us", "us_per_layer"):
+            m = re.search(rf'"{key}": ([0-9.]+)', txt)
+            bench[key] = float(m.group(1)) if m else None
     os.makedirs(PROFILES, exist_ok=True)
     out = os.path.join(PROFILES, f"{KERNEL_NAME}_{workload}_stats.txt")
     lines = [
         f"# rocprofv3 kernel statistics, workload {workload}",
         f"# command: rocprofv3 --kernel-trace --stats -d STATS_DIR -o run --output-format csv -- "
-        f"python3 bench.py --workload {workload} --steps {steps} --warmup 100 --no-secondary "
-        f"--no-cpu-baseline --no-next-rows",
-        f"# summary: python3 bench.py --workload {workload} --steps {steps} --stats-summary STATS_DIR",
+        f"python3 bench.py --gpus 1 --steps {steps} --warmup {warmup}",
+        f"# summary: python3 bench.py --workload {workload} --steps {steps} --warmup {warmup} "
+        f"--stats-summary STATS_DIR",
         "",
         "kernel | calls | average us | min us | max us",
     ]
@@ -616,14 +774,92 @@ def stats_summary(stats_dir, workload, steps):
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f}")
     lines += [
         "",
-        f"{KERNEL_NAME}, timed fused-forward loop ({len(fused)} launches, no cache flush): "
-        f"average {statistics.mean(fused):.2f} us",
-        f"{KERNEL_NAME}, kernel-alone loop ({len(alone)} launches, 512 MiB evicting read before each): "
-        f"average {statistics.mean(alone):.2f} us, median {statistics.median(alone):.2f} us",
-        f"one {KERNEL_NAME} dispatch per tree_attn_partials call (the masked part rides on the "
-        f"last split)",
-        f"bench.py kernel_avg_us (HIP events around the same tree_attn_partials calls): {bench_avg}",
+        f"headline layer, {KERNEL_NAME}, timed fused-forward loop ({len(fused)} launches, back to "
+        f"back, no cache flush): average {statistics.mean(fused):.2f} us, median "
+        f"{statistics.median(fused):.2f} us",
+        f"headline layer, {KERNEL_NAME}, kernel-alone loop ({len(alone)} launches, 512 MiB "
+        f"evicting read before each): average {statistics.mean(alone):.2f} us, median "
+        f"{statistics.median(alone):.2f} us",
+        f"bench.py in the same run: kernel_avg_us {bench.get('kernel_avg_us')} (HIP events around "
+        f"the kernel-alone calls), us_per_layer {bench.get('us_per_layer')} (wall, timed forwards)",
+        "",
+        "every forward step of the fresh process (first W warm-up, then the S timed): prefix "
+        "kernel us | combine (merge kernel) us | start-to-start step us",
     ]
+    for k, a, m, st in step_rows:
+        tag = "warm-up" if k < W else "timed"
+        lines.append(f"step {k:3d} ({tag}): {a:8.2f} | {m if m is None else round(m, 2)} | "
+                     f"{st if st is None else round(st, 2)}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def clock_summary(clk_dir, workload, steps, warmup):
+    """Shader clock of every headline dispatch from a rocprofv3 --pmc GRBM_COUNT GRBM_GUI_ACTIVE
+    pass. GRBM_COUNT ticks once per shader clock on each of the eight XCDs, over a window that is
+    the dispatch's duration plus a fixed profiler overhead. The overhead and the clock of light
+    kernels come from the two lightly loaded kernels of the run -- the 512 MiB evicting read (a
+    memory-bound torch reduction, ~140 us) and the merge (~11 us) -- taken at one clock f:
+    count = overhead + 8 f duration. Each prefix dispatch then runs at (GRBM_COUNT - overhead) /
+    8 / duration."""
+    paths = glob.glob(os.path.join(clk_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no counter collection under {clk_dir}")
+    by = {}
+    with open(paths[0]) as f:
+        for r in csv.DictReader(f):
+            d = by.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"],
+                                                 "s": int(r["Start_Timestamp"]),
+                                                 "e": int(r["End_Timestamp"])})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    ds = sorted(by.values(), key=lambda d: d["s"])
+    red = [d for d in ds if "reduce_kernel" in d["name"]]
+    if not red:
+        raise SystemExit("no evicting reads (reduce_kernel) to calibrate against")
+    mrg = [d for d in ds if "merge_kernel" in d["name"]]
+    if not mrg:
+        raise SystemExit("no merge dispatches to calibrate against")
+    # two light kernels of very different lengths at one clock f: count = over + 8 f t
+    tr_, cr = (statistics.median(d["e"] - d["s"] for d in red),
+               statistics.median(d["GRBM_COUNT"] for d in red))
+    tm, cm = (statistics.median(d["e"] - d["s"] for d in mrg),
+              statistics.median(d["GRBM_COUNT"] for d in mrg))
+    f_light = (cr - cm) / 8 / (tr_ - tm)
+    over = cm - 8 * f_light * tm
+
+    def ghz(d):
+        return (d["GRBM_COUNT"] - over) / 8 / (d["e"] - d["s"])
+
+    pre = [d for d in ds if KERNEL_NAME in d["name"]]
+    W, S = warmup, steps
+    fused, alone = pre[:W + S], pre[2 * W + S:2 * W + 2 * S]
+    lines = [
+        f"# shader clock of the headline prefix-kernel dispatches, workload {workload}",
+        f"# command: rocprofv3 --pmc GRBM_COUNT GRBM_GUI_ACTIVE --kernel-trace -d CLK_DIR -o run "
+        f"--output-format csv -- python3 bench.py --gpus 1 --steps {steps} --warmup {warmup} "
+        f"--no-configs --no-next-rows --no-cpu-baseline --no-secondary",
+        f"# summary: python3 bench.py --workload {workload} --steps {steps} --warmup {warmup} "
+        f"--clock-summary CLK_DIR",
+        f"# counter dispatches run one at a time with idle gaps between them, so the clocks here "
+        f"are those of a lightly loaded part; fitted over the evicting reads and the merges: "
+        f"light-kernel clock {f_light:.3f} GHz, GRBM_COUNT overhead per dispatch {over:.0f}",
+        "",
+        "dispatch | duration us | shader cycles per XCD | clock GHz",
+    ]
+    for k, d in enumerate(fused + alone):
+        tag = ("forward warm-up" if k < W else "forward timed" if k < W + S else
+               "kernel alone")
+        cyc = (d["GRBM_COUNT"] - over) / 8
+        lines.append(f"{tag} {k:2d} | {(d['e'] - d['s']) / 1e3:8.2f} | {cyc:9.0f} | {ghz(d):.3f}")
+    cyc = [(d["GRBM_COUNT"] - over) / 8 for d in fused + alone]
+    lines += ["", f"median shader cycles per dispatch: {statistics.median(cyc):.0f} "
+                  f"(= {statistics.median(cyc) / 2.4e3:.1f} us at the 2.4 GHz top clock)",
+              f"median clock: {statistics.median(ghz(d) for d in fused + alone):.3f} GHz",
+              "evicting reads (torch reduction over 512 MiB): median "
+              f"{statistics.median((d['e'] - d['s']) / 1e3 for d in red):.1f} us"]
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"{KERNEL_NAME}_{workload}_clock.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -664,17 +900,17 @@ def workload_table(steps, warmup, seed):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa_64k_pinned")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the drawn-length (32k..64k) variant of the workload")
+                    help="skip the unfused breakdown of the headline layer")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing every configuration (the configs entry)")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip timing greedy acceptance and the KV commit")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run plain 1 GiB copies (reference for HBM counters)")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--parse-util", metavar="UTIL_DIR",
                     help="summarise a rocprofv3 --pmc pass of the utilisation counters")
@@ -684,15 +920,20 @@ def main():
                     help="summarise a rocprofv3 --stats run of --next-rows-only into profiles/")
     ap.add_argument("--stats-summary", metavar="STATS_DIR",
                     help="write the text summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--clock-summary", metavar="CLK_DIR",
+                    help="summarise a rocprofv3 --pmc GRBM_COUNT GRBM_GUI_ACTIVE pass")
     ap.add_argument("--table", action="store_true",
                     help="time every bf16 workload (fused forward and split step) and print a "
                          "table row for each instead of the JSON line")
     args = ap.parse_args()
 
     if args.stats_summary:
-        stats_summary(args.stats_summary, args.workload, args.steps)
+        stats_summary(args.stats_summary, args.workload, args.steps, args.warmup)
         return
 
+    if args.clock_summary:
+        clock_summary(args.clock_summary, args.workload, args.steps, args.warmup)
+        return
     if args.accept_stats_summary:
         accept_stats_summary(args.accept_stats_summary, args.steps)
         return
@@ -776,37 +1017,16 @@ def main():
     if not args.no_secondary and wl.name == "gqa_64k_pinned":
         print("[bench] unfused breakdown", file=sys.stderr, flush=True)
         line["breakdown"] = time_breakdown(case, max(5, args.steps // 5), 3)
-        wl2 = inputs.WORKLOADS["gqa_64k"]
-        case2 = inputs.make_case(wl2, args.seed, pad="finite")
-        w2 = work_of(case2)
-        r2 = time_case(case2, args.steps, args.warmup, wl2.name)
-        ms2 = r2["wall_s"] * 1e3 / args.steps
-        line["secondary"] = {"workload": "GQA bf16, 64-node tree, prefix lengths drawn in [32k, 64k]",
-                             "prefix_lens": case2.seq_lens.tolist(),
-                             "us_per_layer": round(ms2 * 1e3, 2),
-                             "tb_per_s": round(w2["step_bytes"] / (ms2 * 1e-3) / 1e12, 4),
-                             "kernel_avg_us": round(statistics.mean(r2["kernel_us"]), 2)}
-        del case2
-        torch.cuda.empty_cache()
-        # the same layer with its prefix in a page pool (64-key pages in random order)
-        case3 = inputs.make_case(wl, args.seed, layout="paged", page_size=64, pad="finite")
-        r3 = time_case(case3, args.steps, args.warmup, "gqa_64k_pinned paged")
-        ms3 = r3["wall_s"] * 1e3 / args.steps
-        line["paged"] = {"workload": "the headline layer, prefix in a pool of 64-key pages "
-                                     "(random page order, block table per sequence)",
-                         "us_per_layer": round(ms3 * 1e3, 2),
-                         "tb_per_s": round(work["step_bytes"] / (ms3 * 1e-3) / 1e12, 4),
-                         "kernel_avg_us": round(statistics.mean(r3["kernel_us"]), 2)}
-        del case3
-        torch.cuda.empty_cache()
+    if not args.no_configs:
+        line["configs"] = time_configs(args.steps, args.warmup, args.seed)
     if not args.no_next_rows and wl.name == "gqa_64k_pinned":
         line["next_rows"] = time_next_rows(args.steps, args.warmup, args.seed)
         torch.cuda.empty_cache()
-    if args.copy_calibration:
-        copy_calibration()
+    line["copy_ceiling"] = copy_ceiling()
     if not args.no_cpu_baseline:
-        threads = min(16, len(os.sched_getaffinity(0)))
+        threads = len(os.sched_getaffinity(0))
         line["cpu_baseline"] = cpu_baseline(case, threads)
+        line["cpu_baseline"].update(host_cpu())
     print(json.dumps(line), flush=True)
 
 

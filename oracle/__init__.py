@@ -112,7 +112,7 @@ def attend(*, q, k_cache, v_cache, seq_lens, k_tree, v_tree, parent, scale, dtyp
     o = np.zeros((n, D), dtype=np.float64)
     lse = np.zeros(n, dtype=np.float64)
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = len(os.sched_getaffinity(0)) or 1   # the cores this process may run on
     rc = _load().oracle_attend(B, T, Hq, Hkv, D, dt, float(scale), _ptr(q_), _ptr(kc), _ptr(vc),
                                Lmax, _ptr(seq_lens), _ptr(block_table), int(page_size),
                                max_blocks, num_pages, _ptr(kt), _ptr(vt), _ptr(parent),

@@ -132,6 +132,42 @@ def test_forward_argument_errors(lib):
                                 None) == _lib.TA_EINVAL
 
 
+@pytest.mark.parametrize("page_size,max_blocks", [
+    (24, 4),            # not a power of two
+    (8, 4),             # below 16 keys
+    (-(1 << 31), 4),    # negative
+    ((1 << 30) + 1, 1),  # above 2^30 (the page shift's range)
+    (1 << 16, 1 << 16),  # capacity max_blocks * page_size past INT32_MAX
+    (64, 0),            # no block-table entries
+])
+def test_paged_parameters_rejected_by_every_entry_point(lib, page_size, max_blocks):
+    """A block table with bad paging parameters is refused on the host by every entry point that
+    plans the split -- the tree-only call, the workspace / split queries and the combine included,
+    none of which reads the prefix -- before any capacity or page shift is computed from it."""
+    p = problem(block_table=FAKE, page_size=page_size, max_blocks=max_blocks, num_pages=4)
+    o = ctypes.c_void_p(FAKE)
+    n = ctypes.c_size_t(0)
+    k = ctypes.c_int(0)
+    assert lib.tree_attn_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.TA_EINVAL
+    assert lib.tree_attn_num_splits(ctypes.byref(p), ctypes.byref(k)) == _lib.TA_EINVAL
+    assert lib.tree_attn_tree(ctypes.byref(p), o, o, None, None) == _lib.TA_EINVAL
+    assert lib.tree_attn_combine(ctypes.byref(p), o, 1 << 30, o, o, None) == _lib.TA_EINVAL
+    assert lib.tree_attn_forward(ctypes.byref(p), o, o, o, 1 << 30, None, None) == _lib.TA_EINVAL
+    assert lib.tree_attn_partials(ctypes.byref(p), o, 1 << 30, None, None) == _lib.TA_EINVAL
+    assert lib.tree_kv_commit(ctypes.byref(p), o, o, o, o, o, None, None) == _lib.TA_EINVAL
+    # B = 0 plans nothing but is still refused with such parameters
+    p0 = problem(B=0, block_table=FAKE, page_size=page_size, max_blocks=max_blocks, num_pages=4)
+    assert lib.tree_attn_workspace_size(ctypes.byref(p0), ctypes.byref(n)) == _lib.TA_EINVAL
+
+
+def test_largest_page_size_plans(lib):
+    """Pages of 2^30 keys are admitted (one block-table entry) and plan without overflow."""
+    p = problem(block_table=FAKE, page_size=1 << 30, max_blocks=1, num_pages=1)
+    k = ctypes.c_int(0)
+    assert lib.tree_attn_num_splits(ctypes.byref(p), ctypes.byref(k)) == _lib.TA_OK
+    assert k.value >= 1
+
+
 def test_merge_and_mask_argument_errors(lib):
     o = ctypes.c_void_p(1 << 20)
     assert lib.tree_attn_merge(1, 2, 3, 96, o, o, o, o, o, 0, o, None) == _lib.TA_EUNSUPPORTED

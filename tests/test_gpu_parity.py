@@ -5,7 +5,9 @@ inputs max |dO| <= 1e-4 and max |dLSE| <= 1e-4 (fp32 accumulation over at most a
 terms per lane, errors ~1e-6). Inputs are the generator's seeded cases; padding rows are NaN so
 that any read past a sequence's length shows up as a NaN in the output.
 """
+import os
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -49,16 +51,33 @@ def run_forward(case, **kw):
     return out.float().cpu().numpy(), lse.cpu().numpy(), int(err.item())
 
 
-def check(case, o_gpu, lse_gpu, o_ref, lse_ref, what):
+def check(case, o_gpu, lse_gpu, o_ref, lse_ref, what, rows=None):
+    """Bars of the module docstring over the given rows; prints the worst row of each."""
     atol_o, atol_l = TOL[case.dtype]
     o_gpu = o_gpu.reshape(o_ref.shape)
     lse_gpu = lse_gpu.reshape(lse_ref.shape)
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
     fin = np.isfinite(lse_ref)
     assert np.array_equal(np.isfinite(lse_gpu), fin), f"{what}: -inf pattern differs"
-    do = np.abs(o_gpu - o_ref).max() if o_ref.size else 0.0
-    dl = np.abs(lse_gpu[fin] - lse_ref[fin]).max() if fin.any() else 0.0
-    say(f"{what}: max|dO|={do:.3e} max|dLSE|={dl:.3e}")
+    B, T, Hq = case.q.shape[:3]
+
+    def name(k):
+        if rows is not None:
+            return tuple(int(x) for x in rows[k])
+        return (int(k // (T * Hq)), int(k // Hq % T), int(k % Hq))
+
+    do = dl = 0.0
+    wo = wl_ = "-"
+    if o_ref.size:
+        e = np.abs(o_gpu - o_ref).reshape(len(lse_ref), -1).max(axis=1)
+        k = int(np.argmax(e))
+        do, wo = float(e[k]), name(k)
+    if fin.any():
+        e = np.where(fin, np.abs(np.where(fin, lse_gpu, 0) - np.where(fin, lse_ref, 0)), 0)
+        k = int(np.argmax(e))
+        dl, wl_ = float(e[k]), name(k)
+    say(f"{what}: {len(lse_ref)} rows, max|dO|={do:.3e} at (b,i,h)={wo}, "
+        f"max|dLSE|={dl:.3e} at {wl_}")
     assert do <= atol_o, f"{what}: max|dO| {do} > {atol_o}"
     assert dl <= atol_l, f"{what}: max|dLSE| {dl} > {atol_l}"
 
@@ -316,46 +335,125 @@ def test_determinism():
 
 
 # ------------------------------------------------------------------------------------------------
-# full configuration sizes, sampled rows, in the default launch plan
+# full configuration sizes, in the default launch plan (the one bench.py times)
+#
+# Every output row is compared for the headline layer (every prefix 64k), the drawn-length GQA
+# layer (contiguous and paged), the long-reasoning layer, the MHA layer and the sweep's small
+# trees. The larger sweep trees and the beam tree are compared on at least two rows of every
+# 32-row wavefront tile of every (sequence, KV head, row block). The oracle runs on every core this
+# process may use; its results are kept for the module, so the layouts and the unfused calls of
+# one workload share them.
 
 
-def sample_rows(case, n_per_b=12, seed=0):
+def oracle_threads():
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+_CASES = {}
+_REFS = {}
+
+
+def full_case(name, layout="contiguous"):
+    key = (name, layout)
+    if key not in _CASES:
+        _CASES.clear()   # one full-size case on the host at a time
+        _CASES[key] = inputs.make_case(inputs.WORKLOADS[name], 0, layout=layout, page_size=64)
+    return _CASES[key]
+
+
+def oracle_ref(name, which="full", rows=None):
+    """The oracle on the contiguous case of ``name`` (seed 0): every row, or ``rows``. The paged
+    case of the same seed holds the same values (tests/test_oracle_pins.py pins paged = contiguous
+    for the oracle), so one result checks both layouts."""
+    key = (name, which, None if rows is None else rows.tobytes())
+    if key not in _REFS:
+        case = full_case(name)
+        t0 = time.perf_counter()
+        _REFS[key] = oracle.attend_case(case, which=which, rows=rows, nthreads=oracle_threads())
+        n = len(_REFS[key][1])
+        say(f"oracle {name}/{which}: {n} rows in {time.perf_counter() - t0:.1f} s on "
+            f"{oracle_threads()} threads")
+    return _REFS[key]
+
+
+def tile_rows(case, seed=0):
+    """At least two rows of every 32-row wavefront tile of every (sequence, KV head, row block).
+    Packed row r = node * G + member of KV head g is query head g * G + member of that node; the
+    first pick walks the lane position across tiles, the second is drawn."""
+    B, T, Hq, Hkv = case.wl.B, case.wl.T, case.wl.Hq, case.wl.Hkv
+    G, R = Hq // Hkv, T * (Hq // Hkv)
     rng = np.random.default_rng(seed)
-    B, T, Hq = case.wl.B, case.wl.T, case.wl.Hq
-    rows = []
+    rows = set()
     for b in range(B):
-        picks = {(0, 0), (T - 1, Hq - 1)}
-        while len(picks) < min(n_per_b, T * Hq):
-            picks.add((int(rng.integers(T)), int(rng.integers(Hq))))
-        rows += [(b, i, h) for i, h in sorted(picks)]
-    return np.array(rows, dtype=np.int32)
+        for g in range(Hkv):
+            for w0 in range(0, R, 32):
+                n = min(32, R - w0)
+                for r in (w0 + (7 * b + 5 * g + 3 * (w0 // 32)) % n, w0 + int(rng.integers(n))):
+                    node, m = divmod(r, G)
+                    rows.add((b, node, g * G + m))
+    return np.array(sorted(rows), dtype=np.int32)
 
 
-FULL = ["mha_7b", "gqa_64k", "gqa_64k_pinned", "sweep_t1", "sweep_t6", "sweep_t16", "sweep_t32",
-        "sweep_t64", "sweep_t128", "long_reasoning", "gqa_64k_beam"]
+def compare_rows(case, o, lse, rows, ref, what):
+    B, T, Hq, D = case.q.shape
+    if rows is None:
+        check(case, o.reshape(-1, D), lse.reshape(-1), ref[0], ref[1], what)
+    else:
+        idx = (rows[:, 0] * T + rows[:, 1]) * Hq + rows[:, 2]
+        check(case, o.reshape(-1, D)[idx], lse.reshape(-1)[idx], ref[0], ref[1], what,
+              rows=rows)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), f"{what}: non-finite rows"
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_forward_full_size_sampled(name):
-    w = inputs.WORKLOADS[name]
-    case = inputs.make_case(w, 0)
-    say(f"full {name}: lens={case.seq_lens.tolist()}")
+ALL_ROWS = ["gqa_64k_pinned", "gqa_64k", "long_reasoning", "mha_7b", "sweep_t1", "sweep_t6",
+            "sweep_t16"]
+TILE_ROWS = ["sweep_t32", "sweep_t64", "sweep_t128", "gqa_64k_beam"]
+
+
+@pytest.mark.parametrize("name", ALL_ROWS)
+def test_forward_full_size_every_row(name):
+    case = full_case(name)
+    say(f"full {name}: lens={case.seq_lens.tolist()}, all {case.q.shape[0] * case.q.shape[1] * case.q.shape[2]} rows")
     o, lse, err = run_forward(case)
     assert err == 0
-    rows = sample_rows(case)
-    o_ref, lse_ref = oracle.attend_case(case, rows=rows)
-    B, T, Hq, D = case.q.shape
-    idx = (rows[:, 0] * T + rows[:, 1]) * Hq + rows[:, 2]
-    check(case, o.reshape(-1, D)[idx], lse.reshape(-1)[idx], o_ref, lse_ref, f"full {name}")
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    compare_rows(case, o, lse, None, oracle_ref(name), f"full {name}")
 
 
-def test_forward_full_paged_gqa_sampled():
-    case = inputs.make_case(inputs.WORKLOADS["gqa_64k"], 1, layout="paged", page_size=64)
+@pytest.mark.parametrize("name", ["gqa_64k", "gqa_64k_pinned"])
+def test_forward_full_size_paged_every_row(name):
+    """The same layers with their prefixes in a pool of 64-key pages in random order."""
+    case = full_case(name, "paged")
+    say(f"full {name} paged: lens={case.seq_lens.tolist()}")
     o, lse, err = run_forward(case)
     assert err == 0
-    rows = sample_rows(case, seed=1)
-    o_ref, lse_ref = oracle.attend_case(case, rows=rows)
-    B, T, Hq, D = case.q.shape
-    idx = (rows[:, 0] * T + rows[:, 1]) * Hq + rows[:, 2]
-    check(case, o.reshape(-1, D)[idx], lse.reshape(-1)[idx], o_ref, lse_ref, "full gqa paged")
+    compare_rows(case, o, lse, None, oracle_ref(name), f"full {name} paged")
+
+
+@pytest.mark.parametrize("name", TILE_ROWS)
+def test_forward_full_size_every_tile(name):
+    case = full_case(name)
+    rows = tile_rows(case)
+    say(f"full {name}: lens={case.seq_lens.tolist()}, {len(rows)} rows over every wavefront tile")
+    o, lse, err = run_forward(case)
+    assert err == 0
+    compare_rows(case, o, lse, rows, oracle_ref(name, rows=rows), f"full {name}")
+
+
+def test_unfused_calls_full_size():
+    """tree_attn_prefix, tree_attn_tree and tree_attn_merge on the headline layer, every row,
+    against the oracle's prefix-only, tree-only and whole results."""
+    name = "gqa_64k_pinned"
+    case = full_case(name)
+    g = to_gpu(case)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o_c, l_c = _lib.prefix(g["q"], g["k_cache"], g["v_cache"], g["seq_lens"], scale=case.scale,
+                           err=err)
+    o_s, l_s = _lib.tree(g["q"], g["k_tree"], g["v_tree"], g["parent"], scale=case.scale,
+                         err=err)
+    o_m, l_m = _lib.merge(o_c, l_c, o_s, l_s, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    del g
+    for o, l, which in ((o_c, l_c, "prefix"), (o_s, l_s, "tree"), (o_m, l_m, "full")):
+        compare_rows(case, o.float().cpu().numpy(), l.cpu().numpy(), None,
+                     oracle_ref(name, which), f"unfused {which} {name}")

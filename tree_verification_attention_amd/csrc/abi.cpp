@@ -75,6 +75,14 @@ int check_shape(const ta_problem *p) {
     if (p->Hq < 1 || p->Hkv < 1 || p->Hq % p->Hkv || p->Hkv > 4096) return TA_EINVAL;
     if (!(p->scale > 0.f) || !isfinite(p->scale)) return TA_EINVAL;
     if (p->num_splits < 0) return TA_EINVAL;
+    // the paged parameters feed the split plan of every entry point (the capacity
+    // max_blocks * page_size, the page shift), tree-only calls included
+    if (p->block_table) {
+        const int ps = p->page_size;
+        if (ps < 16 || ps > (1 << 30) || (ps & (ps - 1)) || p->max_blocks < 1 || p->num_pages < 1)
+            return TA_EINVAL;
+        if ((int64_t)p->max_blocks * ps > INT32_MAX) return TA_EINVAL;
+    }
     if (p->B == 0) return TA_OK;
     const int es = elem_size(p->dtype);
     if (!p->q || !aligned16(p->q)) return TA_EINVAL;
@@ -89,11 +97,7 @@ int check_prefix(const ta_problem *p) {
     if (!p->seq_lens) return TA_EINVAL;
     if (!stride_ok(p->kv_s0, es) || !stride_ok(p->kv_s1, es) || !stride_ok(p->kv_s2, es))
         return TA_EINVAL;
-    if (p->block_table) {
-        const int ps = p->page_size;
-        if (ps < 16 || (ps & (ps - 1)) || p->max_blocks < 1 || p->num_pages < 1) return TA_EINVAL;
-        if ((int64_t)p->max_blocks * ps > INT32_MAX) return TA_EINVAL;
-    } else if (p->Lmax < 0) {
+    if (!p->block_table && p->Lmax < 0) {
         return TA_EINVAL;
     }
     if (!p->k_cache || !p->v_cache || !aligned16(p->k_cache) || !aligned16(p->v_cache))
@@ -117,9 +121,10 @@ int check_tree(const ta_problem *p) {
     return TA_OK;
 }
 
+// log2 of a power of two in [1, 2^30] (check_shape admits no other page size)
 int ilog2(int x) {
     int s = 0;
-    while ((1 << s) < x) ++s;
+    while (s < 30 && (1 << s) < x) ++s;
     return s;
 }
 
@@ -127,7 +132,7 @@ Plan make_plan(const ta_problem *p) {
     Plan pl;
     const int G = p->Hq / p->Hkv;
     const int R = p->T * G;
-    pl.capacity = p->block_table ? p->max_blocks * p->page_size : p->Lmax;
+    pl.capacity = p->block_table ? (int)((int64_t)p->max_blocks * p->page_size) : p->Lmax;
     if (pl.capacity < 0) pl.capacity = 0;
     pl.rows = (int64_t)p->B * p->T * p->Hq;
     int64_t wg_per_split;

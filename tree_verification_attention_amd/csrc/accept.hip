@@ -7,8 +7,8 @@
 // root-attached node) and its parent is accepted; the deepest accepted node ends the committed
 // path, and the greedy token of its row is emitted as the correction token.
 //
-// argmax_kernel: every logits row is cut into chunks of 64 KB, one workgroup each, every thread
-// holding 16 16-byte loads in flight (vocabularies of 1e5+ entries make this the HBM-bound part).
+// argmax_kernel: every logits row is cut into chunks of 32 KB, one workgroup each, every thread
+// holding 8 16-byte loads in flight (vocabularies of 1e5+ entries make this the HBM-bound part).
 // Each thread scans its entries in increasing index order keeping the first maximum; winners
 // merge by (larger value, then smaller index) and each chunk's winner goes to the workspace. NaN
 // never wins; a row of NaN only gives 0.
