@@ -17,7 +17,8 @@
  * Conventions shared by every call:
  *   - Pointers are device pointers unless stated otherwise. The caller allocates and owns all
  *     memory, including the workspace; the library allocates nothing, keeps no pointer after a
- *     call returns and holds no mutable global state.
+ *     call returns and holds no mutable global state -- except tree_attn_forward_noalloc, whose
+ *     partials live in one fixed device array per GPU (see there).
  *   - All work is enqueued on ``stream`` (0 = the null stream); no call synchronises the host.
  *   - Return values are ta_status codes. Argument errors are reported before anything is
  *     enqueued. Errors that only the device can see (a parent index out of range, a prefix
@@ -45,7 +46,9 @@ typedef enum ta_status {
     TA_EINVAL = 1,        /* null pointer, bad shape, stride or alignment, Hq % Hkv != 0, T > 256 */
     TA_EUNSUPPORTED = 2,  /* head_dim not in {64, 128}, unknown dtype */
     TA_EWORKSPACE = 3,    /* workspace missing or smaller than tree_attn_workspace_size() */
-    TA_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+    TA_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
+    TA_ESCRATCH = 5       /* tree_attn_forward_noalloc: the problem's split partials need more
+                             than TA_NOALLOC_SCRATCH_BYTES */
 } ta_status;
 
 typedef enum ta_dtype {
@@ -171,6 +174,25 @@ int tree_attn_merge(int B, int T, int Hq, int D, const float *o_a, const float *
  */
 int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t ws_bytes,
                       int32_t *err_flag, hipStream_t stream);
+
+/* Bytes of the device array that tree_attn_forward_noalloc keeps its split partials in. */
+#define TA_NOALLOC_SCRATCH_BYTES (96u << 20)
+
+/*
+ * tree_attn_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same computation, the
+ * same kernels and the same results, with the workspace replaced by one file-scope device array
+ * of TA_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds from the library's load
+ * until the process ends. The call allocates nothing and calls no allocating routine; its first
+ * call on a device looks the array's address up (hipGetSymbolAddress). Returns TA_ESCRATCH, with
+ * nothing enqueued, when the problem needs more than that (tree_attn_workspace_size() above
+ * TA_NOALLOC_SCRATCH_BYTES; at D = 128, 96 MiB holds up to 32 768 output rows with two splits
+ * or 8192 rows with eight). Every call on one GPU shares the array and leaves its contents
+ * there: calls that overlap on one GPU (other streams or host threads) race, and the caller
+ * serialises them. Arguments and the other errors as for tree_attn_forward.
+ */
+int tree_attn_forward_noalloc(const ta_problem *p, void *o, float *lse, int32_t *err_flag,
+                              hipStream_t stream);
 
 /*
  * The divide step of tree_attn_forward on its own: every prefix part and the masked tree part

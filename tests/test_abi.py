@@ -39,8 +39,8 @@ def test_every_declared_function_is_exported(lib):
 
 def test_status_strings_and_version(lib):
     assert lib.tree_attn_abi_version() == 100
-    for code in range(5):
-        assert _lib.status_string(code)
+    for code in range(6):
+        assert _lib.status_string(code) != "unknown status"
     assert _lib.status_string(99) == "unknown status"
 
 
@@ -166,6 +166,27 @@ def test_largest_page_size_plans(lib):
     k = ctypes.c_int(0)
     assert lib.tree_attn_num_splits(ctypes.byref(p), ctypes.byref(k)) == _lib.TA_OK
     assert k.value >= 1
+
+
+def test_noalloc_forward_rejects_problems_beyond_its_scratch(lib):
+    """The allocation-free forward refuses, on the host and before any launch, a problem whose
+    split partials need more than its fixed device array; argument errors come first."""
+    T, Hq, Hkv, L = 256, 32, 8, 16384
+    big = problem(B=16, T=T, Hq=Hq, Hkv=Hkv, Lmax=L, q_sb=T * Hq * 128, q_st=Hq * 128,
+                  kv_s0=L * Hkv * 128, kv_s1=Hkv * 128, kt_sb=T * Hkv * 128, kt_st=Hkv * 128)
+    rc, need = ws_size(lib, big)
+    assert rc == _lib.TA_OK and need > _lib.TA_NOALLOC_SCRATCH_BYTES
+    o = ctypes.c_void_p(FAKE)
+    assert lib.tree_attn_forward_noalloc(ctypes.byref(big), o, o, None, None) == _lib.TA_ESCRATCH
+    assert "TA_NOALLOC_SCRATCH_BYTES" in _lib.status_string(_lib.TA_ESCRATCH)
+    assert lib.tree_attn_forward_noalloc(ctypes.byref(problem(D=96)), o, o, None,
+                                         None) == _lib.TA_EUNSUPPORTED
+    assert lib.tree_attn_forward_noalloc(ctypes.byref(problem(B=0)), o, o, None, None) == 0
+    # the headline layer (4 x 64 nodes x 32 heads, 8 splits) fits
+    hl = problem(B=4, T=64, Hq=32, Hkv=8, Lmax=65536, q_sb=64 * 32 * 128, q_st=32 * 128,
+                 kv_s0=65536 * 8 * 128, kv_s1=8 * 128, kt_sb=64 * 8 * 128, kt_st=8 * 128)
+    rc, need = ws_size(lib, hl)
+    assert rc == _lib.TA_OK and need <= _lib.TA_NOALLOC_SCRATCH_BYTES
 
 
 def test_merge_and_mask_argument_errors(lib):

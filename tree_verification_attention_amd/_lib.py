@@ -16,7 +16,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtreeattn.so")
 
-TA_OK, TA_EINVAL, TA_EUNSUPPORTED, TA_EWORKSPACE, TA_EHIP = range(5)
+TA_OK, TA_EINVAL, TA_EUNSUPPORTED, TA_EWORKSPACE, TA_EHIP, TA_ESCRATCH = range(6)
+TA_NOALLOC_SCRATCH_BYTES = 96 << 20
 TA_BF16, TA_F32 = 0, 1
 TA_DEV_BAD_PARENT, TA_DEV_BAD_LEN, TA_DEV_BAD_PAGE, TA_DEV_BAD_COMMIT, TA_DEV_BAD_TOKEN = 1, 2, 4, 8, 16
 TA_MAX_TREE = 256
@@ -28,7 +29,7 @@ EXPORTS = ("tree_mask_build", "tree_attn_workspace_size", "tree_attn_num_splits"
            "tree_attn_status_string", "tree_attn_abi_version", "tree_greedy_accept",
            "tree_greedy_accept_workspace_size", "tree_spec_sample",
            "tree_spec_sample_workspace_size", "tree_gdn_verify", "tree_gdn_commit",
-           "tree_kv_commit")
+           "tree_kv_commit", "tree_attn_forward_noalloc")
 
 
 class TreeAttnError(RuntimeError):
@@ -78,6 +79,7 @@ def load(path: str = LIB_PATH):
     lib.tree_attn_tree.argtypes = [PP, P, P, P, P]
     lib.tree_attn_merge.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P]
     lib.tree_attn_forward.argtypes = [PP, P, P, P, S, P, P]
+    lib.tree_attn_forward_noalloc.argtypes = [PP, P, P, P, P]
     lib.tree_attn_partials.argtypes = [PP, P, S, P, P]
     lib.tree_attn_combine.argtypes = [PP, P, S, P, P, P]
     lib.tree_attn_workspace_lse_offset.argtypes = [PP, ctypes.POINTER(S)]
@@ -203,6 +205,19 @@ def forward(q, k_cache, v_cache, seq_lens, k_tree, v_tree, parent, *, block_tabl
     _check("tree_attn_forward", load().tree_attn_forward(
         ctypes.byref(p), _gpu(out, "out", q.dtype), _gpu(lse, "lse", torch.float32),
         _gpu(ws, "workspace"), nbytes, _gpu(err, "err", torch.int32), _stream()))
+    return out, lse
+
+
+def forward_noalloc(q, k_cache, v_cache, seq_lens, k_tree, v_tree, parent, *, out, lse,
+                    block_table=None, page_size=None, scale=None, num_splits: int = 0, err=None):
+    """tree_attn_forward_noalloc: the forward with its partials in the library's fixed device
+    array (no workspace); the caller passes the outputs, so nothing is allocated here either."""
+    p = make_problem(q, k_cache, v_cache, seq_lens, k_tree, v_tree, parent,
+                     block_table=block_table, page_size=page_size, scale=scale,
+                     num_splits=num_splits)
+    _check("tree_attn_forward_noalloc", load().tree_attn_forward_noalloc(
+        ctypes.byref(p), _gpu(out, "out", q.dtype), _gpu(lse, "lse", torch.float32),
+        _gpu(err, "err", torch.int32), _stream()))
     return out, lse
 
 

@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libtreeattn.so")
 SOURCES = ["abi.cpp", "attn_prefix.hip", "attn_f32.hip", "mask_merge.hip", "accept.hip",
-           "spec.hip", "gdn.hip"]
+           "spec.hip", "gdn.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

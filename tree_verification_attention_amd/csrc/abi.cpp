@@ -279,6 +279,9 @@ const char *tree_attn_status_string(int status) {
         case TA_EUNSUPPORTED: return "unsupported head_dim or dtype";
         case TA_EWORKSPACE: return "workspace missing or too small";
         case TA_EHIP: return "HIP runtime or kernel launch failure";
+        case TA_ESCRATCH:
+            return "problem needs more split-partial space than the allocation-free entry point "
+                   "holds (TA_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
