@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 METRIC = "tree-verify attention µs/layer + achieved HBM TB/s, 64-node tree @64k ctx"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+FP32_PEAK_TFS = 157.3        # MI355X fp32 vector
 KERNEL_NAME = "attn_prefix_kernel"
 COPY_BYTES = 1 << 30
 FLUSH_BYTES = 1 << 29
@@ -409,7 +410,7 @@ def time_next_rows(steps, warmup, seed):
         return statistics.mean(a.elapsed_time(b) * 1e3 for a, b in evs)
 
     print("[bench] greedy acceptance", file=sys.stderr, flush=True)
-    acc_ws = torch.empty(_lib.greedy_accept_workspace_size(lg.dtype, B, T, V), dtype=torch.uint8,
+    acc_ws = torch.zeros(_lib.greedy_accept_workspace_size(lg.dtype, B, T, V), dtype=torch.uint8,
                          device="cuda")
     acc_us = timed(lambda: _lib.greedy_accept(lg, draft, parent, ws=acc_ws))
     _, n_gpu, path_gpu, _ = _lib.greedy_accept(lg, draft, parent)
@@ -455,7 +456,9 @@ def time_next_rows(steps, warmup, seed):
             while j >= 0:
                 pairs += 1
                 j = int(gc.parent[b, j])
-    gdn_flops = GHv * (B * 4 * GT * Gd * Gd + pairs * (4 * Gd + 4 * Gd))
+    gdn_mfma_flops = GHv * B * 4 * GT * Gd * Gd           # K S0 and Q S0: bf16 MFMA
+    gdn_valu_flops = GHv * pairs * (4 * Gd + 4 * Gd)       # path coefficients and terms: fp32
+    gdn_flops = gdn_mfma_flops + gdn_valu_flops
     gdn_bytes = (gc.q.nbytes + gc.k.nbytes + gc.v.nbytes + gc.g.nbytes + gc.beta.nbytes
                  + gc.parent.nbytes + gc.S0.nbytes + B * GT * GHv * Gd * 4)
     t0 = time.perf_counter()
@@ -503,9 +506,7 @@ def time_next_rows(steps, warmup, seed):
             "workload": f"B={B}, T={GT} bounded tree, H_k={GHk}, H_v={GHv}, d_k=d_v={Gd}, "
                         "bf16 q/k/v, fp32 states",
             "us": round(gdn_us, 2), "algorithmic_flops": gdn_flops,
-            "achieved_tflops": round(gdn_flops / (gdn_us * 1e-6) / 1e12, 2),
-            "peak_tflops": 157.3, "bound": "alu (fp32)",
-            "frac": round(gdn_flops / (gdn_us * 1e-6) / 1e12 / 157.3, 4),
+            **gdn_roofline(gdn_us, gdn_mfma_flops, gdn_valu_flops, gdn_bytes),
             "bytes": gdn_bytes, "cpu_oracle_s": round(gdn_cpu_s, 3)},
         "gdn_commit": {
             "workload": f"B={B}, H_v={GHv}, d_k=d_v={Gd} fp32 states, {int(gn.sum())} accepted "
@@ -519,6 +520,24 @@ def time_next_rows(steps, warmup, seed):
             "us": round(com_us, 2), "algorithmic_bytes": com_bytes,
             "note": "latency-bound: a few hundred KB move per call"},
     }
+
+
+def gdn_roofline(us, mfma_flops, valu_flops, nbytes):
+    """Each resource of the GDN verify kernel against its own peak: the K S0 / Q S0 products
+    (counted once, though the kernel runs each as two bf16 MFMAs for the high and low halves of
+    S0) against the dense bf16 MFMA peak, the fp32 path terms against the fp32 vector peak, the
+    bytes against HBM; ``frac`` is the largest, ``bound`` names it."""
+    t = us * 1e-6
+    parts = {"mfma_bf16": mfma_flops / t / 1e12 / MFMA_BF16_PEAK_TFS,
+             "valu_fp32": valu_flops / t / 1e12 / FP32_PEAK_TFS,
+             "hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
+    bound = max(parts, key=parts.get)
+    return {"mfma_tflops": round(mfma_flops / t / 1e12, 2), "mfma_peak_tflops": MFMA_BF16_PEAK_TFS,
+            "valu_tflops": round(valu_flops / t / 1e12, 2), "valu_peak_tflops": FP32_PEAK_TFS,
+            "achieved_gbs": round(nbytes / t / 1e9, 1), "peak_gbs": HBM_PEAK_GBS,
+            "fracs": {k: round(v, 4) for k, v in parts.items()}, "bound": bound,
+            "frac": round(parts[bound], 4),
+            "note": "latency-bound: every resource well below its peak"}
 
 
 def pct(xs, q):
@@ -682,7 +701,7 @@ def accept_stats_summary(stats_dir, steps):
     with open(paths[0]) as f:
         stats = list(csv.DictReader(f))
     names = ("argmax_kernel", "accept_kernel", "spec_mass_kernel", "spec_walk_kernel",
-             "gdn_verify_kernel", "commit_kernel", "lens_kernel")
+             "gdn_verify_kernel", "gdn_commit_kernel", "commit_kernel")
     rows = [r for r in stats if any(n in r["Name"] for n in names)]
     bench = None
     logs = glob.glob(stats_dir.rstrip("/") + ".log")
@@ -713,8 +732,8 @@ def accept_stats_summary(stats_dir, steps):
                       f"{ACCEPT_BYTES / us / 1e3:.1f} GB/s ({ACCEPT_BYTES / us / 1e3 / HBM_PEAK_GBS:.3f} "
                       f"of {HBM_PEAK_GBS:.0f} GB/s); every call follows a 512 MiB evicting read"]
     if bench:
-        lines.append(f"bench.py next-row timings (HIP events around each call): "
-                     f"{json.dumps(bench)}")
+        lines.append(f"bench.py next-row timings of the same run, under the tracer (HIP events "
+                     f"around each call): {json.dumps(bench)}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))

@@ -338,7 +338,8 @@ int tree_gdn_commit(const void *k, const void *v, const float *g, const float *b
  * k_cache / v_cache are the writable buffers that p->k_cache / p->v_cache describe. A sequence
  * whose commit would pass the capacity (or with accept_len outside [0, T]) writes nothing, keeps
  * its length and sets TA_DEV_BAD_COMMIT; a path entry outside [0, T) sets it and is skipped.
- * new_seq_lens may alias p->seq_lens (it is written after every copy has read the old lengths).
+ * new_seq_lens may alias p->seq_lens (one workgroup per sequence reads its old length, then
+ * writes the new one). One kernel launch.
  */
 int tree_kv_commit(const ta_problem *p, void *k_cache, void *v_cache, const int32_t *path,
                    const int32_t *accept_len, int32_t *new_seq_lens, int32_t *err_flag,

@@ -129,6 +129,26 @@ def test_greedy_accept_f32_special_rows():
     check_accept(case, "f32 special rows")
 
 
+def test_greedy_accept_one_workspace_many_sizes():
+    """One workspace serves calls of different sizes one after another (larger, smaller, larger
+    again, a single node): each call only reads the chunk winners it wrote, so every call matches
+    the oracle whatever the previous one left there."""
+    sizes = [(4, 64, 128256, "bf16"), (2, 16, 3000, "bf16"), (6, 100, 50000, "f32"),
+             (3, 1, 776, "bf16"), (4, 64, 128256, "bf16")]
+    need = max(_lib.greedy_accept_workspace_size(torch.bfloat16 if dt == "bf16" else torch.float32,
+                                                 B, T, V) for B, T, V, dt in sizes)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for k, (B, T, V, dt) in enumerate(sizes):
+        case = inputs.make_accept_case(B, T, V, 20 + k, dtype=dt)
+        g, n, path, nxt = _lib.greedy_accept(dev(case.logits), dev(case.draft), dev(case.parent),
+                                             ws=ws)
+        torch.cuda.synchronize()
+        rg, rn, rpath, rnxt = A.greedy_accept(case.logits, case.draft, case.parent, case.dtype)
+        say(f"shared workspace call {k}: B={B} T={T} V={V} {dt} accept_len {n.tolist()[:6]}")
+        assert np.array_equal(g.cpu().numpy(), rg) and np.array_equal(n.cpu().numpy(), rn)
+        assert np.array_equal(path.cpu().numpy(), rpath) and np.array_equal(nxt.cpu().numpy(), rnxt)
+
+
 def test_greedy_accept_rejects_a_short_workspace():
     case = inputs.make_accept_case(4, 64, 128256, 2)
     lg = dev(case.logits)

@@ -17,8 +17,8 @@
 //
 // Commit (same page, reserve / execute / commit: only the accepted prefix's target KV is
 // committed): commit_kernel copies the path's tree K/V rows to cache positions L, L + 1, ... of
-// the sequence (contiguous or paged); lens_kernel then advances the lengths. A commit that would
-// pass the cache capacity writes nothing and keeps the length.
+// the sequence (contiguous or paged) and advances its length, one workgroup per sequence in one
+// launch. A commit that would pass the cache capacity writes nothing and keeps the length.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -313,56 +313,73 @@ __global__ __launch_bounds__(TA_MAX_TREE) void accept_kernel(const int2 *part, i
     }
 }
 
-// Block (slot j, kv-head g, sequence b): copies tree K/V row path[b][j] to cache position
-// seq_lens[b] + j, 16 bytes per thread.
-__global__ __launch_bounds__(64) void commit_kernel(CommitArgs c) {
-    const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+// One workgroup per sequence b: copies the tree K/V rows path[b][0 .. n-1] of every KV head to
+// cache positions seq_lens[b] .. seq_lens[b] + n - 1, then writes the new length. Each thread
+// moves up to kCommitVec 16-byte pieces per round, all loads issued before any store (a typical
+// commit -- a few rows of a few KV heads -- is one round). The workgroup is the only reader of
+// seq_lens[b] and writes new_lens[b] after a barrier that follows its read, so new_lens may alias
+// seq_lens in the same launch.
+constexpr int kCommitThreads = 512;
+constexpr int kCommitVec = 4;
+
+__global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitArgs c, int Hkv,
+                                                                int32_t *new_lens) {
+    const int b = blockIdx.x;
     const int n = c.accept_len[b];
     const int L = c.seq_lens[b];
-    if (j >= n) return;
-    if (L < 0 || L > c.capacity) {
-        if (c.err && threadIdx.x == 0) atomicOr(c.err, (int32_t)TA_DEV_BAD_LEN);
-        return;
+    __syncthreads();  // every thread has read the old length before it is overwritten below
+    const bool len_ok = L >= 0 && L <= c.capacity;
+    const bool fits = n >= 0 && n <= c.T && L + n <= c.capacity;
+    if (threadIdx.x == 0 && c.err && n > 0) {
+        if (!len_ok) atomicOr(c.err, (int32_t)TA_DEV_BAD_LEN);
+        else if (!fits) atomicOr(c.err, (int32_t)TA_DEV_BAD_COMMIT);
     }
-    if (n > c.T || L + n > c.capacity) {
-        if (c.err && threadIdx.x == 0 && j == 0) atomicOr(c.err, (int32_t)TA_DEV_BAD_COMMIT);
-        return;
-    }
-    const int node = c.path[(int64_t)b * c.T + j];
-    if (node < 0 || node >= c.T) {
-        if (c.err && threadIdx.x == 0) atomicOr(c.err, (int32_t)TA_DEV_BAD_COMMIT);
-        return;
-    }
-    const int pos = L + j;
-    int64_t dst;
-    if (c.block_table) {
-        const int pg = c.block_table[(int64_t)b * c.max_blocks + (pos >> c.page_shift)];
-        if ((unsigned)pg >= (unsigned)c.num_pages) {
-            if (c.err && threadIdx.x == 0) atomicOr(c.err, (int32_t)TA_DEV_BAD_PAGE);
-            return;
+    if (len_ok && fits) {
+        const int chunks = c.row_bytes / 16;            // 16-byte pieces of one K (or V) row
+        const int per_slot = Hkv * 2 * chunks;          // every KV head, K then V
+        const int total = n * per_slot;
+        for (int base = 0; base < total; base += kCommitThreads * kCommitVec) {
+            uint4 val[kCommitVec];
+            char *dst_p[kCommitVec];
+#pragma unroll
+            for (int u = 0; u < kCommitVec; ++u) {
+                dst_p[u] = nullptr;
+                const int t = base + u * kCommitThreads + threadIdx.x;
+                if (t >= total) continue;
+                const int j = t / per_slot;
+                int r = t - j * per_slot;
+                const int g = r / (2 * chunks);
+                r -= g * 2 * chunks;
+                const bool v = r >= chunks;
+                const int q = v ? r - chunks : r;
+                const int node = c.path[(int64_t)b * c.T + j];
+                if (node < 0 || node >= c.T) {
+                    if (c.err && q == 0 && !v) atomicOr(c.err, (int32_t)TA_DEV_BAD_COMMIT);
+                    continue;
+                }
+                const int pos = L + j;
+                int64_t dst;
+                if (c.block_table) {
+                    const int pg = c.block_table[(int64_t)b * c.max_blocks + (pos >> c.page_shift)];
+                    if ((unsigned)pg >= (unsigned)c.num_pages) {
+                        if (c.err && q == 0 && !v) atomicOr(c.err, (int32_t)TA_DEV_BAD_PAGE);
+                        continue;
+                    }
+                    dst = pg * c.kv_s0 + (pos & c.page_mask) * c.kv_s1 + g * c.kv_s2;
+                } else {
+                    dst = b * c.kv_s0 + (int64_t)pos * c.kv_s1 + g * c.kv_s2;
+                }
+                const int64_t src = b * c.kt_sb + (int64_t)node * c.kt_st + g * c.kt_sh;
+                val[u] = *reinterpret_cast<const uint4 *>(
+                    static_cast<const char *>(v ? c.vt : c.kt) + src * c.es + 16 * q);
+                dst_p[u] = static_cast<char *>(v ? c.vc : c.kc) + dst * c.es + 16 * q;
+            }
+#pragma unroll
+            for (int u = 0; u < kCommitVec; ++u)
+                if (dst_p[u]) *reinterpret_cast<uint4 *>(dst_p[u]) = val[u];
         }
-        dst = pg * c.kv_s0 + (pos & c.page_mask) * c.kv_s1 + g * c.kv_s2;
-    } else {
-        dst = b * c.kv_s0 + (int64_t)pos * c.kv_s1 + g * c.kv_s2;
     }
-    const int64_t src = b * c.kt_sb + (int64_t)node * c.kt_st + g * c.kt_sh;
-    const int chunks = c.row_bytes / 16;
-    for (int t = threadIdx.x; t < 2 * chunks; t += 64) {
-        const bool v = t >= chunks;
-        const int q = v ? t - chunks : t;
-        const char *s = static_cast<const char *>(v ? c.vt : c.kt) + src * c.es + 16 * q;
-        char *d = static_cast<char *>(v ? c.vc : c.kc) + dst * c.es + 16 * q;
-        *reinterpret_cast<uint4 *>(d) = *reinterpret_cast<const uint4 *>(s);
-    }
-}
-
-__global__ void lens_kernel(const int32_t *seq_lens, const int32_t *accept_len, int B, int T,
-                            int capacity, int32_t *new_lens) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= B) return;
-    const int L = seq_lens[b], n = accept_len[b];
-    const bool ok = L >= 0 && L <= capacity && n >= 0 && n <= T && L + n <= capacity;
-    new_lens[b] = ok ? L + n : L;
+    if (threadIdx.x == 0) new_lens[b] = len_ok && fits ? L + n : L;
 }
 
 }  // namespace
@@ -391,11 +408,7 @@ hipError_t launch_greedy_accept(const void *logits, bool bf16, int64_t row_strid
 }
 
 hipError_t launch_commit(const CommitArgs &c, int B, int Hkv, int32_t *new_lens, hipStream_t s) {
-    hipLaunchKernelGGL(commit_kernel, dim3(c.T, Hkv, B), dim3(64), 0, s, c);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lens_kernel, dim3((B + 255) / 256), dim3(256), 0, s, c.seq_lens,
-                       c.accept_len, B, c.T, c.capacity, new_lens);
+    hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(kCommitThreads), 0, s, c, Hkv, new_lens);
     return hipGetLastError();
 }
 
