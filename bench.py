@@ -79,6 +79,11 @@ def work_of(case):
             "flops": flops, "sum_len": sum_l}
 
 
+def bound_of(flops, nbytes):
+    """The resource whose peak takes longer for this much work: "mfma" (bf16 dense) or "hbm"."""
+    return "mfma" if flops / (MFMA_BF16_PEAK_TFS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9) else "hbm"
+
+
 def to_device(case):
     import numpy as np
     import torch
@@ -288,10 +293,17 @@ def time_configs(steps, warmup, seed):
             e["tflops"] = round(w["flops"] / (f * 1e-6) / 1e12, 1)
             e["frac_mfma"] = round(w["flops"] / (f * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
             e["split_frac_mfma"] = round(w["flops"] / (k * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
-            e["bound"] = ("mfma" if w["flops"] / MFMA_BF16_PEAK_TFS > w["step_bytes"] / HBM_PEAK_GBS
-                          / 1e3 else "hbm")
+            e["bound"] = bound_of(w["flops"], w["step_bytes"])
         else:
             e["bound"] = "latency (fp32 path, 0.15 MB)"
+        if layout == "contiguous":
+            # HBM traffic and counter shares of the split step, where profiles/ holds them for
+            # the kernel as it stands
+            t, u = traffic_entry(name), util_entry(name)
+            if t:
+                e["split_traffic_bytes"] = round(t["traffic_bytes"])
+            if u:
+                e["split_counters"] = u
         out[key] = e
         print(f"[bench] {key}: {f:.1f} us/layer (split {k:.1f} us), "
               f"{e['tb_per_s']:.2f} TB/s", file=sys.stderr, flush=True)
@@ -596,36 +608,96 @@ def traffic_entry(workload):
 
 UTIL_COUNTERS = ("MfmaUtil", "LdsBankConflict", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
                  "SQ_WAVES")
+# where the cycles go: MFMA busy, VALU / LDS issue, waits, per SIMD (a second pass)
+ISSUE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                  "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY",
+                  "SQ_INSTS_VALU_TRANS_F32", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
+N_XCD, N_SIMD = 8, 1024
 
 
-def parse_util(util_dir, workload):
-    """Per-dispatch averages of the utilisation counters of the dominant kernel (one rocprofv3
-    --pmc pass of UTIL_COUNTERS) into a text summary under profiles/."""
+def pmc_command(counters, out_dir, workload):
+    return (f"rocprofv3 --pmc {' '.join(counters)} -d {out_dir} -o run --output-format csv -- "
+            f"python3 bench.py --workload {workload} --steps 4 --warmup 1 --no-secondary "
+            f"--no-configs --no-cpu-baseline --no-next-rows")
+
+
+def util_path(workload):
+    return os.path.join(PROFILES, f"{KERNEL_NAME}_{workload}_util.txt")
+
+
+def parse_util(util_dirs, workload):
+    """Per-dispatch averages of the dominant kernel's counters from the utilisation pass
+    (UTIL_COUNTERS) and the issue pass (ISSUE_COUNTERS), with the per-SIMD cycle shares derived
+    from them, into a text summary under profiles/."""
     vals = {}
-    for path in glob.glob(os.path.join(util_dir, "**", "*counter_collection.csv"), recursive=True):
-        with open(path) as f:
-            for row in csv.DictReader(f):
-                if KERNEL_NAME in row["Kernel_Name"]:
-                    vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    for d in util_dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    if KERNEL_NAME in row["Kernel_Name"]:
+                        vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
     if not vals:
-        raise SystemExit(f"no {KERNEL_NAME} dispatches under {util_dir}")
+        raise SystemExit(f"no {KERNEL_NAME} dispatches under {' '.join(util_dirs)}")
+    m = {k: statistics.mean(v) for k, v in vals.items()}
     os.makedirs(PROFILES, exist_ok=True)
-    out = os.path.join(PROFILES, f"{KERNEL_NAME}_{workload}_util.txt")
     lines = [
-        f"# rocprofv3 utilisation counters of {KERNEL_NAME}, workload {workload}, mean per dispatch",
-        f"# command: rocprofv3 --pmc {' '.join(UTIL_COUNTERS)} -d UTIL_DIR -o run "
-        f"--output-format csv -- python3 bench.py --workload {workload} --steps 4 --warmup 1 "
-        f"--no-secondary --no-cpu-baseline --no-next-rows",
-        f"# summary: python3 bench.py --workload {workload} --parse-util UTIL_DIR",
+        f"# rocprofv3 counters of {KERNEL_NAME} (one tree_attn_partials call), workload {workload}, "
+        f"mean per dispatch",
+        f"# utilisation pass: {pmc_command(UTIL_COUNTERS, 'UTIL_DIR', workload)}",
+        f"# issue pass:       {pmc_command(ISSUE_COUNTERS, 'ISSUE_DIR', workload)}",
+        f"# summary: python3 bench.py --workload {workload} --parse-util UTIL_DIR ISSUE_DIR",
+        f"# kernel sources sha256: {kernel_source_hash()}",
         "",
     ]
     for k in sorted(vals):
-        lines.append(f"{k}: {statistics.mean(vals[k]):.6g} ({len(vals[k])} dispatches)")
+        lines.append(f"{k}: {m[k]:.6g} ({len(vals[k])} dispatches)")
+    derived = {}
+    if "GRBM_GUI_ACTIVE" in m:
+        cyc = m["GRBM_GUI_ACTIVE"] / N_XCD          # counted once per XCD
+        derived["cycles per dispatch (GRBM_GUI_ACTIVE / 8 XCDs)"] = cyc
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            derived["MFMA busy share per SIMD"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / cyc
+        if "SQ_ACTIVE_INST_VALU" in m:               # quad-cycles, summed over waves
+            derived["VALU issue share per SIMD"] = 4 * m["SQ_ACTIVE_INST_VALU"] / N_SIMD / cyc
+        if "SQ_ACTIVE_INST_LDS" in m:
+            derived["LDS issue share per SIMD"] = 4 * m["SQ_ACTIVE_INST_LDS"] / N_SIMD / cyc
+        if "SQ_WAVE_CYCLES" in m and "SQ_WAVES" in m:
+            derived["wave lifetime share (wave-cycles / waves / cycles)"] = (
+                4 * m["SQ_WAVE_CYCLES"] / m["SQ_WAVES"] / cyc)
+    if "SQ_WAIT_INST_ANY" in m and "SQ_WAVE_CYCLES" in m:
+        derived["wave-cycles waiting to issue (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)"] = (
+            m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"])
+    if "SQ_INSTS_VALU_TRANS_F32" in m and "SQ_INSTS_VALU" in m:
+        derived["transcendental share of VALU instructions"] = (
+            m["SQ_INSTS_VALU_TRANS_F32"] / m["SQ_INSTS_VALU"])
+    if derived:
+        lines += ["", "derived:"] + [f"  {k}: {v:.4g}" for k, v in derived.items()]
     lines += ["", "MfmaUtil: percent of the cycles the MFMA units were busy; LdsBankConflict: percent of",
-              "LDS active cycles lost to bank conflicts (rocprofv3 derived metrics)."]
-    with open(out, "w") as f:
+              "LDS active cycles lost to bank conflicts (rocprofv3 derived metrics). SQ_ACTIVE_INST_*",
+              "and SQ_WAVE_CYCLES count quad-cycles summed over waves; SQ_VALU_MFMA_BUSY_CYCLES counts",
+              "cycles summed over the 1024 SIMDs; GRBM_GUI_ACTIVE counts cycles summed over the 8 XCDs."]
+    with open(util_path(workload), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def util_entry(workload):
+    """MFMA utilisation and the derived shares of a util summary, or None (absent or taken
+    before the kernel sources last changed)."""
+    path = util_path(workload)
+    if not os.path.exists(path):
+        return None
+    out, sha = {}, None
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("# kernel sources sha256:"):
+                sha = ln.split(":", 1)[1].strip()
+            elif ln.startswith("MfmaUtil:") and ln.rstrip().endswith("dispatches)"):
+                out["mfma_util_pct"] = float(ln.split()[1])
+            elif ln.strip().startswith(("MFMA busy share", "VALU issue share", "LDS issue share")):
+                k, v = ln.strip().rsplit(":", 1)
+                out[k.split(" share")[0].lower().replace(" ", "_") + "_share"] = float(v)
+    return out if sha == kernel_source_hash() else None
 
 
 def parse_pmc(fetch_dir, write_dir, workload):
@@ -653,7 +725,8 @@ def parse_pmc(fetch_dir, write_dir, workload):
         # the 1 GiB calibration copies: the largest copy dispatches (input uploads are tiny)
         xs = [(k, v) for k, v in vals if "copy" in k.lower()]
         if not xs:
-            raise SystemExit("no copy dispatches in the counters (run with --copy-calibration)")
+            raise SystemExit("no copy dispatches in the counters (bench.py's copy-ceiling leg "
+                             "makes them)")
         top = max(v for _, v in xs)
         big = [v for _, v in xs if v >= 0.9 * top]
         return statistics.mean(big), len(big), xs[0][0]
@@ -674,15 +747,14 @@ def parse_pmc(fetch_dir, write_dir, workload):
     entry["traffic_bytes"] = entry["fetch_bytes"] + entry["write_bytes"]
     os.makedirs(PROFILES, exist_ok=True)
     out = traffic_path(workload)
-    run = (f"python3 bench.py --workload {workload} --steps 4 --warmup 1 --no-secondary "
-           f"--no-cpu-baseline --no-next-rows --copy-calibration")
     with open(out, "w") as f:
         f.write(f"# HBM traffic of one tree_attn_partials call (one {KERNEL_NAME} dispatch: the "
                 f"prefix splits and the masked part) on workload {workload}.\n"
-                f"# FETCH pass: rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- {run}\n"
-                f"# WRITE pass: rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR -o run --output-format csv -- {run}\n"
+                f"# FETCH pass: {pmc_command(['FETCH_SIZE'], 'FETCH_DIR', workload)}\n"
+                f"# WRITE pass: {pmc_command(['WRITE_SIZE'], 'WRITE_DIR', workload)}\n"
                 f"# summary:    python3 bench.py --workload {workload} --parse-pmc FETCH_DIR WRITE_DIR\n"
-                f"# Counter KiB are scaled by bytes / KiB-read of the plain 1 GiB copy in the same runs.\n")
+                f"# Counter KiB are scaled by bytes / KiB-read of the plain 1 GiB copies in the same "
+                f"runs (the copy-ceiling leg).\n")
         json.dump(entry, f, indent=1)
         f.write("\n")
     print(json.dumps(entry, indent=1))
@@ -814,6 +886,95 @@ def stats_summary(stats_dir, workload, steps, warmup):
     print("\n".join(lines))
 
 
+def power_trace(seconds, seed):
+    """The headline forward back to back for ``seconds`` from a fresh process: per-step HIP
+    event times, the first 400 one by one and all of them in 50 ms buckets of wall-clock time
+    since the first step (printed as one JSON object). Run beside a power / clock sampler to see how the part's power management
+    paces the kernel."""
+    import torch
+
+    from tree_verification_attention_amd import inputs
+
+    case = inputs.make_case(inputs.WORKLOADS["gqa_64k_pinned"], seed, pad="finite")
+    L = Launch(case)
+    torch.cuda.synchronize()
+    batch = 20
+    t_start = time.time()
+    buckets, first = {}, []
+    while time.time() - t_start < seconds:
+        evs = []
+        for _ in range(batch):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(L.stream)
+            L.fwd()
+            e1.record(L.stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        t = time.time() - t_start
+        us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        if len(first) < 400:
+            first.extend(round(x, 1) for x in us)
+        buckets.setdefault(int(t / 0.05), []).extend(us)
+    L.check_flag()
+    return {"t0_unix": t_start, "bucket_s": 0.05, "first_steps_us": first,
+            "buckets": [{"t_s": round(k * 0.05, 3), "steps": len(v),
+                         "median_us": round(statistics.median(v), 1),
+                         "min_us": round(min(v), 1), "max_us": round(max(v), 1)}
+                        for k, v in sorted(buckets.items())]}
+
+
+def power_summary(trace_path, smi_path, seconds):
+    """Text summary of a --power-trace run and of the amd-smi samples taken beside it."""
+    import re
+
+    with open(trace_path) as f:
+        d = json.load(f)
+    first = d["first_steps_us"]
+    smi = []
+    with open(smi_path) as f:
+        parts = re.split(r"^T (\S+)\n", f.read(), flags=re.M)
+    for i in range(1, len(parts), 2):
+        try:
+            j = json.loads(parts[i + 1])
+            g = j["gpu_data"][0] if isinstance(j, dict) else j[0]
+            smi.append((float(parts[i]) - d["t0_unix"], g["power"]["socket_power"]["value"],
+                        g["clock"]["gfx_0"]["clk"]["value"]))
+        except (ValueError, KeyError, IndexError, TypeError):
+            continue
+    lines = [
+        "# the headline forward (tree_attn_forward, workload gqa_64k_pinned) back to back from a "
+        "fresh process, with the part's socket power and shader clock sampled beside it",
+        f"# trace:   python3 bench.py --power-trace {seconds:g} > TRACE_JSON",
+        "# sampler, started just before the trace: for i in $(seq 1 100); do echo \"T $(date "
+        "+%s.%N)\"; amd-smi metric -p -c --json; done > SMI_SAMPLES",
+        f"# summary: python3 bench.py --power-summary TRACE_JSON SMI_SAMPLES {seconds:g}",
+        "",
+        "step times (HIP events on the launch stream), us, steps 0.. in order:",
+    ]
+    for i in range(0, min(len(first), 120), 10):
+        lines.append(f"  {i:3d}: " + " ".join(f"{x:6.1f}" for x in first[i:i + 10]))
+    w = first[5:25]
+    lines += ["", f"steps 5..24 (what a run with 5 warm-up and 20 timed steps times): mean "
+              f"{statistics.mean(w):.1f} us, median {statistics.median(w):.1f} us",
+              "", "median step time per second of the trace:"]
+    per_s = {}
+    for bk in d["buckets"]:
+        per_s.setdefault(int(bk["t_s"]), []).append(bk["median_us"])
+    for k in sorted(per_s):
+        lines.append(f"  second {k}: {statistics.median(per_s[k]):.1f} us")
+    lines += ["", "amd-smi samples (time since the first step, s | socket power W | gfx clock MHz; "
+              "the values refresh about once a second):"]
+    prev = None
+    for t, pw, clk in smi:
+        if (pw, clk) != prev:
+            lines.append(f"  {t:6.2f} | {pw:5} | {clk:5}")
+        prev = (pw, clk)
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"{KERNEL_NAME}_gqa_64k_pinned_power.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def clock_summary(clk_dir, workload, steps, warmup):
     """Shader clock of every headline dispatch from a rocprofv3 --pmc GRBM_COUNT GRBM_GUI_ACTIVE
     pass. GRBM_COUNT ticks once per shader clock on each of the eight XCDs, over a window that is
@@ -931,14 +1092,19 @@ def main():
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip timing greedy acceptance and the KV commit")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--parse-util", metavar="UTIL_DIR",
-                    help="summarise a rocprofv3 --pmc pass of the utilisation counters")
+    ap.add_argument("--parse-util", nargs="+", metavar="DIR",
+                    help="summarise the rocprofv3 --pmc passes of the utilisation and issue "
+                         "counters")
     ap.add_argument("--next-rows-only", action="store_true",
                     help="time only greedy acceptance and the KV commit; print their JSON")
     ap.add_argument("--accept-stats-summary", metavar="STATS_DIR",
                     help="summarise a rocprofv3 --stats run of --next-rows-only into profiles/")
     ap.add_argument("--stats-summary", metavar="STATS_DIR",
                     help="write the text summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--power-trace", type=float, metavar="SECONDS",
+                    help="run the headline forward back to back for SECONDS, print step times")
+    ap.add_argument("--power-summary", nargs=3, metavar=("TRACE_JSON", "SMI_SAMPLES", "SECONDS"),
+                    help="summarise a --power-trace run and its amd-smi samples")
     ap.add_argument("--clock-summary", metavar="CLK_DIR",
                     help="summarise a rocprofv3 --pmc GRBM_COUNT GRBM_GUI_ACTIVE pass")
     ap.add_argument("--table", action="store_true",
@@ -950,6 +1116,9 @@ def main():
         stats_summary(args.stats_summary, args.workload, args.steps, args.warmup)
         return
 
+    if args.power_summary:
+        power_summary(args.power_summary[0], args.power_summary[1], float(args.power_summary[2]))
+        return
     if args.clock_summary:
         clock_summary(args.clock_summary, args.workload, args.steps, args.warmup)
         return
@@ -980,6 +1149,9 @@ def main():
 
     if args.next_rows_only:
         print(json.dumps(time_next_rows(args.steps, args.warmup, args.seed)), flush=True)
+        return
+    if args.power_trace:
+        print(json.dumps(power_trace(args.power_trace, args.seed)), flush=True)
         return
     if args.table:
         workload_table(args.steps, args.warmup, args.seed)
