@@ -854,7 +854,7 @@ def stats_summary(stats_dir, workload, steps, warmup):
     lines = [
         f"# rocprofv3 kernel statistics, workload {workload}",
         f"# command: rocprofv3 --kernel-trace --stats -d STATS_DIR -o run --output-format csv -- "
-        f"python3 bench.py --gpus 1 --steps {steps} --warmup {warmup}",
+        f"python3 bench.py --gpus 1 --steps {steps} --warmup {warmup} > STATS_DIR.log",
         f"# summary: python3 bench.py --workload {workload} --steps {steps} --warmup {warmup} "
         f"--stats-summary STATS_DIR",
         "",
