@@ -17,10 +17,10 @@
 // spec_mass_kernel (data-parallel, HBM-bound): per (row, 4096-entry chunk) of every position
 //   with children, the chunk's sum of [p - q]_+ (N_2's parts: a first rejection there needs it).
 // spec_walk_kernel: G workgroups per sequence, all walking the same tree with the same state.
-//   The per-node values p(x), q(x) are gathered up front, so the walk itself reads LDS only; a
-//   second trial at one position needs N_{k+1} for k >= 2, a pass over that row which the G
-//   workgroups split by chunks and meet on through the workspace; the final token's chunk is
-//   found from the chunk sums, then its owner scans it with a block prefix sum.
+//   The per-node values p(x), q(x) and the acceptance uniforms are gathered up front, so the walk
+//   itself reads LDS only; a second trial at one position needs N_{k+1} for k >= 2, a pass over
+//   that row which the G workgroups split by chunks and meet on through the workspace; the final
+//   token's chunk is found from the chunk sums, then its owner scans it with a block prefix sum.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -109,12 +109,15 @@ __global__ __launch_bounds__(kMassThreads) void spec_mass_kernel(const float *p,
     }
 }
 
+constexpr int kKidWords = TA_MAX_TREE / 64;
+
 struct WalkShared {
-    int32_t par[TA_MAX_TREE];
+    unsigned long long kids[TA_MAX_TREE + 1][kKidWords];  // children of each row, as bit sets
     int32_t first_child[TA_MAX_TREE + 1];
     int32_t next_sib[TA_MAX_TREE];
     float pv[TA_MAX_TREE];             // p(x) and q(x) of every node's draft token at its row
     float qv[TA_MAX_TREE];
+    double ua[TA_MAX_TREE];            // every node's acceptance uniform
     double n2[TA_MAX_TREE + 1];        // N_2 of every row with children
     double cs[TA_MAX_VOCAB / kChunk];  // chunk sums of the current final weights
     double red[kWalkThreads / 64];
@@ -167,16 +170,32 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t row0 = (int64_t)b * (T + 1);
     int32_t *err = a.err;
-    for (int r = tid; r <= T; r += kWalkThreads) sh.first_child[r] = INT32_MAX;
     int pa = -1, x = 0;
+    double ua = 0.0;
     if (tid < T) {
         pa = a.parent[(int64_t)b * T + tid];
         x = a.draft[(int64_t)b * T + tid];
+        ua = a.u_accept[(int64_t)b * T + tid];
+    }
+    // N_2 of every row with children: four threads per row, thread j summing chunks j, j + 4, ...
+    // in order, then two butterfly steps. The first kPre chunk sums of every thread in the first
+    // group of rows are loaded here, before the tree is even known, so that the wait for them
+    // overlaps the gathers and the child lists (a leaf row holds no sums; its total is dropped)
+    constexpr int kRowsPerPass = kWalkThreads / 4, kPre = 8;
+    const int n2_row = tid >> 2, n2_j = tid & 3;
+    double n_pre[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+        const int c = n2_j + 4 * k;
+        n_pre[k] = n2_row <= T && c < nch ? a.sums[(row0 + n2_row) * nch + c] : 0.0;
+    }
+    for (int i = tid; i < (T + 1) * kKidWords; i += kWalkThreads) (&sh.kids[0][0])[i] = 0;
+    if (tid < T) {
         if (pa < -1 || pa >= tid) {
             if (err && g == 0) atomicOr(err, (int32_t)TA_DEV_BAD_PARENT);
             pa = -1;
         }
-        sh.par[tid] = pa;
+        sh.ua[tid] = ua;
         // p(x) and q(x) of the node's draft token, at its parent's row
         const int64_t ro = (row0 + pa + 1) * row_stride;
         if (x >= 0 && x < V) {
@@ -190,31 +209,40 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int
         }
     }
     __syncthreads();
+    // child lists as bit sets: bit i of row pa + 1 for node i; a row's first child is its lowest
+    // bit, a node's next sibling the lowest bit above its own
+    if (tid < T) atomicOr(&sh.kids[pa + 1][tid >> 6], 1ull << (tid & 63));
+    __syncthreads();
+    for (int r = tid; r <= T; r += kWalkThreads) {
+        int fc = -1;
+        for (int w = kKidWords - 1; w >= 0; --w)
+            if (sh.kids[r][w]) fc = 64 * w + __builtin_ctzll(sh.kids[r][w]);
+        sh.first_child[r] = fc;
+    }
     if (tid < T) {
-        atomicMin(&sh.first_child[pa + 1], tid);
         int nx = -1;
-        for (int j = tid + 1; j < T; ++j)
-            if (sh.par[j] == pa) {
-                nx = j;
-                break;
-            }
+        for (int w = kKidWords - 1; w >= tid >> 6; --w) {
+            unsigned long long m = sh.kids[pa + 1][w];
+            if (w == tid >> 6) m &= (tid & 63) == 63 ? 0ull : ~0ull << ((tid & 63) + 1);
+            if (m) nx = 64 * w + __builtin_ctzll(m);
+        }
         sh.next_sib[tid] = nx;
     }
     __syncthreads();
-    // N_2 of every row with children, one wavefront per row: lane l sums chunks l, l + 64, ...,
-    // then a butterfly (T + 1 rows: one more than nodes)
-    for (int r = wave; r <= T; r += kWalkThreads / 64) {
-        const bool has_child = sh.first_child[r] != INT32_MAX;
-        double n = 0.0;
-        if (has_child) {
-            const double *sr = a.sums + (row0 + r) * nch;
-            for (int c = lane; c < nch; c += 64) n += sr[c];
-            n = wave_sum(n);
+    for (int r0 = 0; r0 <= T; r0 += kRowsPerPass) {
+        const int r = r0 + n2_row;
+        const double *sr = a.sums + (row0 + r) * nch;
+        double v = 0.0;
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) {
+            const int c = n2_j + 4 * k;
+            v += r0 == 0 ? n_pre[k] : (r <= T && c < nch ? sr[c] : 0.0);
         }
-        if (lane == 0) {
-            sh.n2[r] = n;
-            if (!has_child) sh.first_child[r] = -1;
-        }
+        if (r <= T)
+            for (int c = n2_j + 4 * kPre; c < nch; c += 4) v += sr[c];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        if (n2_j == 0 && r <= T) sh.n2[r] = sh.first_child[r] >= 0 ? v : 0.0;
     }
     if (tid == 0) {
         sh.pos = -1;
@@ -262,8 +290,7 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int
                     break;
                 }
                 const double R = fmax(0.0, (double)sh.pv[c] - sh.Cprev * (double)sh.qv[c]);
-                const bool accept =
-                    n_next == 0.0 || a.u_accept[(int64_t)b * T + c] * sh.Nk * (double)sh.qv[c] < R;
+                const bool accept = n_next == 0.0 || sh.ua[c] * sh.Nk * (double)sh.qv[c] < R;
                 if (accept) {
                     sh.path[sh.n_path++] = c;
                     sh.pos = c;
@@ -293,19 +320,21 @@ __global__ __launch_bounds__(kWalkThreads) void spec_walk_kernel(SpecArgs a, int
         for (int ch = g; ch < nch; ch += G) {
             const double s = chunk_sum_block(p + ro, q + ro, C, pq, ch, nch, V, sh.red);
             if (tid == 0) {
-                __hip_atomic_store(buf + ch, s, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(buf + ch, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 sh.cs[ch] = s;
             }
         }
         // the peers' chunks: a thread per chunk polls its slot until the owner has written it
-        // (the mass kernel set every slot to -1; sums are >= 0)
+        // (the mass kernel set every slot to -1; sums are >= 0). The slot's value is all that is
+        // handed over, so device-scope relaxed atomics suffice: they bypass the XCD's L2 without
+        // the L2 write-back and invalidation that release / acquire order would add per access
         bool late = false;
         for (int ch = tid; ch < nch; ch += kWalkThreads) {
             if (ch % G == g) continue;
-            double v = __hip_atomic_load(buf + ch, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+            double v = __hip_atomic_load(buf + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             for (int spin = 0; v < 0.0 && spin < kSpinLimit; ++spin) {
                 __builtin_amdgcn_s_sleep(2);
-                v = __hip_atomic_load(buf + ch, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+                v = __hip_atomic_load(buf + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             if (v < 0.0) late = true;
             else sh.cs[ch] = v;
