@@ -175,17 +175,21 @@ def time_case(case, steps, warmup, label):
     for _ in range(warmup):
         L.fwd()
     torch.cuda.synchronize()
-    # timed region: exactly `steps` fused steps
+    # timed region: exactly `steps` fused steps, nothing between them
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        L.fwd()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the per-step spread, from a second pass of `steps` forwards right after the timed one: an
+    # event pair around every step costs the step about 6 us, so the timed pass records none
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(L.stream)
         L.fwd()
         ev[i][1].record(L.stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
     # the dominant kernel alone, same stream, same events; before each launch a 512 MiB read
     # (outside the events) evicts the 256 MB last-level cache and the L2s
@@ -814,8 +818,9 @@ def accept_stats_summary(stats_dir, steps):
 def stats_summary(stats_dir, workload, steps, warmup):
     """Text summary of a rocprofv3 --kernel-trace --stats run of this script's default JSON run:
     the kernel statistics, then the headline layer's loops taken apart by position in the trace
-    (W warm-up forwards, the S timed forwards, W warm-up split steps, the S timed split steps, as
-    time_case issues them), with every forward step of the fresh process listed on its own."""
+    (W warm-up forwards, the S timed forwards, S forwards with per-step events, W warm-up split
+    steps, the S timed split steps, as time_case issues them), with every forward step of the
+    fresh process listed on its own."""
     import re
 
     def one(pattern):
@@ -833,7 +838,7 @@ def stats_summary(stats_dir, workload, steps, warmup):
     W, S = warmup, steps
     fwd_idx = prefix_idx[:W + S]                      # forwards: prefix kernel then merge kernel
     fused = [(spans[i][2] - spans[i][1]) / 1e3 for i in prefix_idx[W:W + S]]
-    alone = [(spans[i][2] - spans[i][1]) / 1e3 for i in prefix_idx[2 * W + S:2 * W + 2 * S]]
+    alone = [(spans[i][2] - spans[i][1]) / 1e3 for i in prefix_idx[2 * W + 2 * S:2 * W + 3 * S]]
     step_rows = []
     for k, i in enumerate(fwd_idx):
         j = i + 1                                     # the combine launch follows on the stream
