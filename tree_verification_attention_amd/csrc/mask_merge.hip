@@ -62,32 +62,6 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs m) {
         return p < n0 ? m.o0 + p * m.so0 + row * D : m.o1 + row * D;
     };
 
-    // The first kBatch parts' slices are loaded before anything else (with the part LSEs), so
-    // that a row with at most kBatch parts waits for memory once; later parts come kBatch at a
-    // time. An empty part (LSE = -inf, weight 0) is loaded but never added: its slot may hold
-    // anything. Parts are added in part order.
-    constexpr int kBatch = 16;
-    auto load_batch = [&](int k0, float (&v)[kBatch][PER_LANE]) {
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            if (k0 + j < n) {
-                const float *op = part_o(k0 + j) + lane * PER_LANE;
-                if constexpr (PER_LANE == 2) {
-                    const float2 x = *reinterpret_cast<const float2 *>(op);
-                    v[j][0] = x.x;
-                    v[j][1] = x.y;
-                } else {
-                    v[j][0] = op[0];
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < PER_LANE; ++e) v[j][e] = 0.f;
-            }
-        }
-    };
-    float v[kBatch][PER_LANE];
-    load_batch(0, v);
-
     float mx = -INFINITY;
     for (int c = 0; c < n; c += 64)
         if (c + lane < n) mx = fmaxf(mx, part_lse(c + lane));
@@ -102,14 +76,16 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs m) {
             const float w = (c + lane < n) ? expf(part_lse(c + lane) - mx) : 0.f;
             total += w;
             const int cn = min(64, n - c);
-            for (int k0 = 0; k0 < cn; k0 += kBatch) {
-                if (c + k0 > 0) load_batch(c + k0, v);
-#pragma unroll
-                for (int j = 0; j < kBatch; ++j) {
-                    const float wk = __shfl(w, (k0 + j) & 63);
-                    if (k0 + j < cn && wk != 0.f)
-#pragma unroll
-                        for (int e = 0; e < PER_LANE; ++e) acc[e] += wk * v[j][e];
+            for (int k = 0; k < cn; ++k) {
+                const float wk = __shfl(w, k);
+                if (wk == 0.f) continue;  // empty part (LSE = -inf): its O is never read
+                const float *op = part_o(c + k) + lane * PER_LANE;
+                if constexpr (PER_LANE == 2) {
+                    const float2 v = *reinterpret_cast<const float2 *>(op);
+                    acc[0] += wk * v.x;
+                    acc[1] += wk * v.y;
+                } else {
+                    acc[0] += wk * op[0];
                 }
             }
         }
