@@ -43,6 +43,11 @@ CASES = [
     ("uniform", dict(B=2, T=100, Hk=1, Hv=3, dk=64, dv=128), {"tree": "uniform"}),
     ("one_node", dict(B=3, T=1, Hk=2, Hv=4, dk=128, dv=32), {"tree": "single"}),
     ("dk64_dv256_t200", dict(B=1, T=200, Hk=1, Hv=2, dk=64, dv=256), {"depth_cap": 24}),
+    # enough (sequence, head, 32-column) blocks for two per CU: 64-column, 512-thread workgroups
+    ("wide_dk64_t128", dict(B=4, T=128, Hk=8, Hv=32, dk=64, dv=128), {}),
+    ("wide_chain_128", dict(B=8, T=128, Hk=4, Hv=16, dk=128, dv=128), {"tree": "chain"}),
+    ("wide_dv256_t100", dict(B=2, T=100, Hk=4, Hv=32, dk=128, dv=256), {"tree": "uniform"}),
+    ("wide_one_node", dict(B=8, T=1, Hk=4, Hv=16, dk=128, dv=128), {"tree": "single"}),
 ]
 
 

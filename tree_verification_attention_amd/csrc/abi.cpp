@@ -503,7 +503,7 @@ int tree_gdn_verify(const void *q, const void *k, const void *v, const float *g,
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S0) || !aligned16(o))
         return TA_EINVAL;
     ta::GdnArgs a{q, k, v, g, beta, parent, S0, B, T, Hk, Hv, dk, dv, scale, o, err_flag};
-    return status(ta::launch_gdn_verify(a, stream));
+    return status(ta::launch_gdn_verify(a, cu_count(), stream));
 }
 
 int tree_gdn_commit(const void *k, const void *v, const float *g, const float *beta, int B,

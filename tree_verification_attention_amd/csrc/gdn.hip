@@ -16,8 +16,10 @@
 // in topological order; it is solved level by level of the tree (all nodes of one depth at once,
 // their ancestors being done), so no state is ever updated and nothing needs rolling back.
 //
-// gdn_verify_kernel: one 256-thread workgroup per (value-column block of 32, value head,
-//   sequence). K S_0 and Q S_0 for all nodes run on bf16 MFMA with S_0 split into a high and a
+// gdn_verify_kernel: one workgroup per (value-column block, value head, sequence): 64 columns and
+//   512 threads when that still gives every CU two workgroups' worth of columns (the tree work --
+//   depths, ancestor tables, path coefficients -- is then done once per 64 columns, and the
+//   grid fits the CUs in one round), else 32 columns and 256 threads. K S_0 and Q S_0 for all nodes run on bf16 MFMA with S_0 split into a high and a
 //   low bf16 part (fp32 accumulation; the split leaves about 2^-16 of S_0's relative precision);
 //   the key dot products of ancestor pairs use the two-term bf16 dot instruction, everything
 //   else is fp32 VALU. K of the head and the pseudo-values U live in LDS (sized for 128 or 256
@@ -36,9 +38,9 @@ namespace ta {
 
 namespace {
 
-constexpr int kGdnThreads = 256;
-constexpr int kColBlock = 32;   // value columns per workgroup
-constexpr int kItemCols = 16;   // columns per (node, half) item
+constexpr int kGdnThreads = 256;  // the commit kernel's workgroup
+constexpr int kColBlock = 32;    // value columns per commit workgroup
+constexpr int kItemCols = 16;    // columns per (node, column group) item
 
 __device__ inline float bf(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -86,7 +88,7 @@ struct TreeLds {
     int32_t max_depth;
 };
 
-// Thread i's node (T <= kGdnThreads): its parent, log-decay and write strength.
+// Thread i's node (T <= the workgroup's threads): its parent, log-decay and write strength.
 struct NodeIn {
     int p;
     float g, beta;
@@ -99,8 +101,9 @@ __device__ inline NodeIn node_in(const int32_t *parent, const float *g, const fl
     return NodeIn{parent[i], g[i * gstride], beta[i * gstride]};
 }
 
+template <int NT>
 __device__ inline int tree_levels(NodeIn in, int T, TreeLds &s, int32_t *err) {
-    static_assert(TA_MAX_TREE <= kGdnThreads, "one node per thread");
+    static_assert(TA_MAX_TREE <= NT, "one node per thread");
     const int tid = threadIdx.x;
     if (tid == 0) s.max_depth = 0;
     if (tid < T) {
@@ -120,9 +123,9 @@ __device__ inline int tree_levels(NodeIn in, int T, TreeLds &s, int32_t *err) {
     for (int span = 1; span < T; span <<= 1) {
         // done once every jump pointer has passed the root
         bool more = false;
-        for (int i = tid; i < T; i += kGdnThreads) more |= s.jmp[cur][i] >= 0;
+        for (int i = tid; i < T; i += NT) more |= s.jmp[cur][i] >= 0;
         if (!__syncthreads_or(more)) break;
-        for (int i = tid; i < T; i += kGdnThreads) {
+        for (int i = tid; i < T; i += NT) {
             const int j = s.jmp[cur][i];
             s.dep[cur ^ 1][i] = s.dep[cur][i] + (j >= 0 ? s.dep[cur][j] : 0);
             s.gs[cur ^ 1][i] = s.gs[cur][i] + (j >= 0 ? s.gs[cur][j] : 0.f);
@@ -133,7 +136,7 @@ __device__ inline int tree_levels(NodeIn in, int T, TreeLds &s, int32_t *err) {
     }
     // the tree's depth: a wavefront maximum, then one LDS atomic per wavefront
     int md = 0;
-    for (int i = tid; i < T; i += kGdnThreads) md = max(md, s.dep[cur][i]);
+    for (int i = tid; i < T; i += NT) md = max(md, s.dep[cur][i]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) md = max(md, __shfl_xor(md, m));
     if ((tid & 63) == 0) atomicMax(&s.max_depth, md);
@@ -141,23 +144,25 @@ __device__ inline int tree_levels(NodeIn in, int T, TreeLds &s, int32_t *err) {
     return cur;
 }
 
-template <int DK, int TMAX>
-__global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
+template <int DK, int TMAX, int CB>
+__global__ __launch_bounds__(CB * 8) void gdn_verify_kernel(GdnArgs a) {
+    constexpr int NT = CB * 8;            // threads: 256 for 32 columns, 512 for 64
+    constexpr int kGroups = CB / kItemCols;  // column groups of a node (solve and output items)
     // keys of the head [T][DK] bf16 and the S_0 column block split into bf16 high and low parts
     // (S0 = hi + lo to about 2^-16 relative), transposed [32][DK]; rows padded by 16 bytes so
     // that lanes reading different rows hit different banks
     constexpr int KS = DK + 8;
     __shared__ __align__(16) uint16_t Ks[TMAX * KS];
-    __shared__ __align__(16) float U[TMAX * kColBlock];    // pseudo-values [T][32]
+    __shared__ __align__(16) float U[TMAX * CB];    // pseudo-values [T][32]
     // coefficients along every node's root path, position m (0 = the node itself, m = its m-th
     // ancestor j_m): XA = b_t e^{G_t - G_j} (k_t . k_j) for m >= 1, YA = e^{G_t - G_j} (q_t . k_j);
     // positions past kAncCap are computed where they are used. XA / YA reuse the S_0 halves'
     // LDS, which is dead once the K S_0 / Q S_0 products are done.
     constexpr int kAncCap = TMAX <= 128 ? 16 : 8;
-    constexpr int kS0Bytes = 2 * kColBlock * KS * 2, kCoefBytes = 2 * TMAX * kAncCap * 4;
+    constexpr int kS0Bytes = 2 * CB * KS * 2, kCoefBytes = 2 * TMAX * kAncCap * 4;
     __shared__ __align__(16) unsigned char s0buf[kS0Bytes > kCoefBytes ? kS0Bytes : kCoefBytes];
     uint16_t *S0hi = reinterpret_cast<uint16_t *>(s0buf);
-    uint16_t *S0lo = S0hi + kColBlock * KS;
+    uint16_t *S0lo = S0hi + CB * KS;
     float *XA = reinterpret_cast<float *>(s0buf);
     float *YA = XA + TMAX * kAncCap;
     __shared__ int16_t anc[TMAX * kAncCap];  // j_m of every node, -1 past the root
@@ -165,25 +170,25 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
     const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hf = lane >> 5;
     const int T = a.T, hk = h / (a.Hv / a.Hk);
-    const int c0 = cb * kColBlock;
+    const int c0 = cb * CB;
     const uint16_t *kg = static_cast<const uint16_t *>(a.k);
     // every load of a thread is issued before any LDS store, so their latencies overlap
-    constexpr int KV = TMAX * (DK / 8) / kGdnThreads;  // 16-byte key chunks per thread
+    constexpr int KV = TMAX * (DK / 8) / NT;  // 16-byte key chunks per thread
     uint4 kc[KV];
 #pragma unroll
     for (int r = 0; r < KV; ++r) {
-        const int idx = tid + r * kGdnThreads, t = min(idx / (DK / 8), T - 1);
+        const int idx = tid + r * NT, t = min(idx / (DK / 8), T - 1);
         kc[r] = *reinterpret_cast<const uint4 *>(
             kg + (((int64_t)b * T + t) * a.Hk + hk) * DK + (idx % (DK / 8)) * 8);
     }
     // S_0 entries (d, c) and (d + 1, c) per thread and step, so that one 32-bit LDS store
     // takes both of their bf16 parts
-    constexpr int SV = DK * kColBlock / (2 * kGdnThreads);
+    constexpr int SV = DK * CB / (2 * NT);
     const float *s0 = a.S0 + ((int64_t)b * a.Hv + h) * DK * a.dv;
     float sx[SV][2];
 #pragma unroll
     for (int r = 0; r < SV; ++r) {
-        const int idx = tid + r * kGdnThreads, d = 2 * (idx / kColBlock), c = idx % kColBlock;
+        const int idx = tid + r * NT, d = 2 * (idx / CB), c = idx % CB;
         sx[r][0] = s0[(int64_t)d * a.dv + c0 + c];
         sx[r][1] = s0[(int64_t)(d + 1) * a.dv + c0 + c];
     }
@@ -192,24 +197,24 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
     // keys and S_0 halves into LDS (the loads above are all in flight by now)
 #pragma unroll
     for (int r = 0; r < KV; ++r) {
-        const int idx = tid + r * kGdnThreads;
+        const int idx = tid + r * NT;
         if (idx / (DK / 8) < T)
             *reinterpret_cast<uint4 *>(Ks + (idx / (DK / 8)) * KS + (idx % (DK / 8)) * 8) = kc[r];
     }
 #pragma unroll
     for (int r = 0; r < SV; ++r) {
-        const int idx = tid + r * kGdnThreads, d = 2 * (idx / kColBlock), c = idx % kColBlock;
+        const int idx = tid + r * NT, d = 2 * (idx / CB), c = idx % CB;
         const __bf16 h0 = (__bf16)sx[r][0], h1 = (__bf16)sx[r][1];
         const __bf16 l0 = (__bf16)(sx[r][0] - (float)h0), l1 = (__bf16)(sx[r][1] - (float)h1);
         *reinterpret_cast<bf16x2 *>(S0hi + c * KS + d) = bf16x2{h0, h1};
         *reinterpret_cast<bf16x2 *>(S0lo + c * KS + d) = bf16x2{l0, l1};
     }
-    const int lv = tree_levels(nin, T, tr, a.err);
+    const int lv = tree_levels<NT>(nin, T, tr, a.err);
     const int32_t *dep = tr.dep[lv];
     const float *G = tr.gs[lv];
     const uint16_t *qg = static_cast<const uint16_t *>(a.q);
     const uint16_t *vg = static_cast<const uint16_t *>(a.v);
-    for (int t = tid; t < T; t += kGdnThreads) {
+    for (int t = tid; t < T; t += NT) {
         int j = t;
         for (int m = 0; m < kAncCap; ++m) {
             anc[t * kAncCap + m] = (int16_t)j;
@@ -217,10 +222,12 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
         }
     }
     __syncthreads();
-    // K S_0 and Q S_0 on v_mfma_f32_32x32x16_bf16, one 32-node tile per wavefront at a time:
-    // lane (l32, hf) supplies node row l32 (A) and value column l32 (B) over k = 16 ks + 8 hf
-    // .. + 7; register r of the result is node 8 (r / 4) + 4 hf + r % 4, column l32
-    for (int nt = wave; nt * 32 < T; nt += kGdnThreads / 64) {
+    // K S_0 and Q S_0 on v_mfma_f32_32x32x16_bf16, one (32-node tile, 32-column tile) per
+    // wavefront at a time: lane (l32, hf) supplies node row l32 (A) and value column col
+    // (B) over k = 16 ks + 8 hf .. + 7; register r of the result is node 8 (r / 4) + 4 hf + r % 4
+    constexpr int kColTiles = CB / 32;
+    for (int pt = wave; pt < ((T + 31) / 32) * kColTiles; pt += NT / 64) {
+        const int nt = pt / kColTiles, col = (pt % kColTiles) * 32 + l32;
         // rows past the tree read its last row; their results are dropped below
         const int row = min(nt * 32 + l32, T - 1);
         const uint16_t *qrow = qg + (((int64_t)b * T + row) * a.Hk + hk) * DK;
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int t = min(nt * 32 + 8 * (r / 4) + 4 * hf + r % 4, T - 1);
-            vv[r] = bf(vg[(((int64_t)b * T + t) * a.Hv + h) * a.dv + c0 + l32]);
+            vv[r] = bf(vg[(((int64_t)b * T + t) * a.Hv + h) * a.dv + c0 + col]);
         }
 #pragma unroll
         for (int ks = 0; ks < DK / 16; ++ks)
@@ -243,8 +250,8 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < DK / 16; ++ks) {
             const int d0 = 16 * ks + 8 * hf;
-            const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(S0hi + l32 * KS + d0);
-            const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(S0lo + l32 * KS + d0);
+            const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(S0hi + col * KS + d0);
+            const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(S0lo + col * KS + d0);
             accK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], bh, accK, 0, 0, 0);
             accK = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], bl, accK, 0, 0, 0);
             accQ = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], bh, accQ, 0, 0, 0);
@@ -256,22 +263,23 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
             if (t < T) {
                 const float eg = __expf(G[t]);
                 // right-hand side w_t = beta_t (v_t - e^{G_t} S_0^T k_t), into U
-                U[t * kColBlock + l32] = tr.beta[t] * (vv[r] - eg * accK[r]);
+                U[t * CB + col] = tr.beta[t] * (vv[r] - eg * accK[r]);
                 // e^{G_t} S_0^T q_t goes to the output, which the last phase completes
-                a.o[(((int64_t)b * T + t) * a.Hv + h) * a.dv + c0 + l32] = eg * accQ[r];
+                a.o[(((int64_t)b * T + t) * a.Hv + h) * a.dv + c0 + col] = eg * accQ[r];
             }
         }
     }
     __syncthreads();  // the S_0 halves are dead from here on: their LDS takes XA / YA
-    // path coefficients: item (t, half) takes the even or odd positions of t's root path
-    for (int it = tid; it < 2 * T; it += kGdnThreads) {
-        const int t = it >> 1, half = it & 1;
+    // path coefficients: item (t, part) takes the positions part, part + kGroups, ... of t's
+    // root path
+    for (int it = tid; it < kGroups * T; it += NT) {
+        const int t = it / kGroups, half = it % kGroups;
         if (half >= dep[t]) continue;
         uint32_t kp[DK / 2], qp[DK / 2];
         load_row<DK>(qp, qg + (((int64_t)b * T + t) * a.Hk + hk) * DK);
         load_row<DK>(kp, Ks + t * KS);
         const float bt = tr.beta[t], gt = G[t];
-        for (int m = half; m < kAncCap; m += 2) {
+        for (int m = half; m < kAncCap; m += kGroups) {
             const int j = anc[t * kAncCap + m];
             if (j < 0) break;
             const float e = __expf(gt - G[j]);
@@ -283,12 +291,12 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
     // forward substitution, one tree level at a time: u_t -= b_t e^{G_t - G_j} (k_t . k_j) u_j
     // over the strict ancestors j (all of shallower levels, hence final)
     for (int level = 2; level <= tr.max_depth; ++level) {
-        for (int it = tid; it < 2 * T; it += kGdnThreads) {
-            const int t = it >> 1, cc = (it & 1) * kItemCols;
+        for (int it = tid; it < kGroups * T; it += NT) {
+            const int t = it / kGroups, cc = (it % kGroups) * kItemCols;
             if (dep[t] != level) continue;
             float u[kItemCols];
 #pragma unroll
-            for (int c = 0; c < kItemCols; ++c) u[c] = U[t * kColBlock + cc + c];
+            for (int c = 0; c < kItemCols; ++c) u[c] = U[t * CB + cc + c];
             // ancestors at path positions 1 .. nd from the tables, four at a time so that their
             // loads overlap; deeper ones (past the tables) one by one with the coefficient on the
             // spot
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
                     x[i] = ok ? XA[t * kAncCap + m0 + i] : 0.f;
 #pragma unroll
                     for (int c4 = 0; c4 < kItemCols / 4; ++c4)
-                        uj[i][c4] = *reinterpret_cast<const float4 *>(U + j * kColBlock + cc + 4 * c4);
+                        uj[i][c4] = *reinterpret_cast<const float4 *>(U + j * CB + cc + 4 * c4);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -323,17 +331,17 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
                     const float x = bt * __expf(gt - G[j]) * dot_reg_lds<DK>(kp, Ks + j * KS);
 #pragma unroll
                     for (int c = 0; c < kItemCols; ++c)
-                        u[c] = fmaf(-x, U[j * kColBlock + cc + c], u[c]);
+                        u[c] = fmaf(-x, U[j * CB + cc + c], u[c]);
                 }
             }
 #pragma unroll
-            for (int c = 0; c < kItemCols; ++c) U[t * kColBlock + cc + c] = u[c];
+            for (int c = 0; c < kItemCols; ++c) U[t * CB + cc + c] = u[c];
         }
         __syncthreads();
     }
     // output: o_t = scale (e^{G_t} S_0^T q_t + sum_{j ancestor or self} e^{G_t - G_j} (q_t . k_j) u_j)
-    for (int it = tid; it < 2 * T; it += kGdnThreads) {
-        const int t = it >> 1, cc = (it & 1) * kItemCols;
+    for (int it = tid; it < kGroups * T; it += NT) {
+        const int t = it / kGroups, cc = (it % kGroups) * kItemCols;
         float *orow = a.o + (((int64_t)b * T + t) * a.Hv + h) * a.dv + c0 + cc;
         float acc[kItemCols];
 #pragma unroll
@@ -356,7 +364,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
                 y[i] = ok ? YA[t * kAncCap + m0 + i] : 0.f;
 #pragma unroll
                 for (int c4 = 0; c4 < kItemCols / 4; ++c4)
-                    uj[i][c4] = *reinterpret_cast<const float4 *>(U + j * kColBlock + cc + 4 * c4);
+                    uj[i][c4] = *reinterpret_cast<const float4 *>(U + j * CB + cc + 4 * c4);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_verify_kernel(GdnArgs a) {
             for (int j = tr.par[anc[t * kAncCap + kAncCap - 1]]; j >= 0; j = tr.par[j]) {
                 const float y = __expf(gt - G[j]) * dot_reg_lds<DK>(qp, Ks + j * KS);
 #pragma unroll
-                for (int c = 0; c < kItemCols; ++c) acc[c] = fmaf(y, U[j * kColBlock + cc + c], acc[c]);
+                for (int c = 0; c < kItemCols; ++c) acc[c] = fmaf(y, U[j * CB + cc + c], acc[c]);
             }
         }
 #pragma unroll
@@ -513,16 +521,24 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_commit_kernel(GdnCommitArgs a
 
 }  // namespace
 
-hipError_t launch_gdn_verify(const GdnArgs &a, hipStream_t s) {
-    // trees of up to 128 nodes take the smaller LDS footprint (two workgroups per CU)
-    const dim3 grid(a.dv / kColBlock, a.Hv, a.B);
+hipError_t launch_gdn_verify(const GdnArgs &a, int cus, hipStream_t s) {
+    // 64-column workgroups (one per CU at most; trees of up to 128 nodes) when 32-column ones
+    // would need two rounds of the CUs or more; otherwise 32 columns, trees of up to 128 nodes
+    // taking the smaller LDS footprint (two workgroups per CU)
+    const bool wide = a.T <= 128 && a.dv % 64 == 0 &&
+                      (int64_t)a.B * a.Hv * (a.dv / 32) >= 2 * (int64_t)cus;
+#define TA_GDN(DK, TM, CBW) \
+    hipLaunchKernelGGL((gdn_verify_kernel<DK, TM, CBW>), dim3(a.dv / CBW, a.Hv, a.B), dim3(CBW * 8), 0, s, a)
     if (a.dk == 128) {
-        if (a.T <= 128) hipLaunchKernelGGL((gdn_verify_kernel<128, 128>), grid, dim3(kGdnThreads), 0, s, a);
-        else hipLaunchKernelGGL((gdn_verify_kernel<128, 256>), grid, dim3(kGdnThreads), 0, s, a);
+        if (wide) TA_GDN(128, 128, 64);
+        else if (a.T <= 128) TA_GDN(128, 128, 32);
+        else TA_GDN(128, 256, 32);
     } else {
-        if (a.T <= 128) hipLaunchKernelGGL((gdn_verify_kernel<64, 128>), grid, dim3(kGdnThreads), 0, s, a);
-        else hipLaunchKernelGGL((gdn_verify_kernel<64, 256>), grid, dim3(kGdnThreads), 0, s, a);
+        if (wide) TA_GDN(64, 128, 64);
+        else if (a.T <= 128) TA_GDN(64, 128, 32);
+        else TA_GDN(64, 256, 32);
     }
+#undef TA_GDN
     return hipGetLastError();
 }
 

@@ -109,7 +109,7 @@ struct GdnCommitArgs {
     int32_t *err;
 };
 
-hipError_t launch_gdn_verify(const GdnArgs &a, hipStream_t s);
+hipError_t launch_gdn_verify(const GdnArgs &a, int cus, hipStream_t s);
 hipError_t launch_gdn_commit(const GdnCommitArgs &a, hipStream_t s);
 
 struct SpecArgs {
