@@ -169,7 +169,8 @@ int tree_attn_merge(int B, int T, int Hq, int D, const float *o_a, const float *
  * The whole hybrid tree attention of one layer: prefix (split over the KV length), masked tree
  * part with the mask derived in-kernel, and the log-sum-exp aggregation of all partials, as
  * tree_attn_partials then tree_attn_combine (bf16: two kernel launches, the masked part riding
- * on the last prefix split). o: [B, T, Hq, D] contiguous, of p->dtype; lse: fp32 [B, T, Hq]
+ * on the last prefix split; fp32 with one split: one launch that writes the output directly, the
+ * workspace checked but unused). o: [B, T, Hq, D] contiguous, of p->dtype; lse: fp32 [B, T, Hq]
  * (natural log).
  */
 int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t ws_bytes,

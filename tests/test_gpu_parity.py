@@ -135,6 +135,12 @@ SMALL = [
     ("single_node", wl(B=3, T=1, tree="single", L=(0, 129)), {}),
     ("star", wl(B=2, T=20, tree="star", L=(64, 64)), {}),
     ("uniform_f32_d128", wl(D=128, T=9, dtype="f32", tree="uniform", L=(1, 300)), {}),
+    # fp32, one split (the single-launch forward): prefixes of 2, 1, 1 and 0 keys, a 256-node chain
+    ("f32_one_split_short_prefixes", wl(B=4, Hq=4, Hkv=1, D=64, T=12, dtype="f32", L=(0, 2)), {}),
+    ("f32_chain_t256", wl(B=1, Hq=2, Hkv=1, D=64, T=256, dtype="f32", tree="chain", L=(100, 100)),
+     {}),
+    ("f32_forced_splits_3", wl(B=2, Hq=4, Hkv=2, D=128, T=16, dtype="f32", L=(0, 500)),
+     {"num_splits": 3}),
     ("forced_splits_1", wl(L=(300, 700)), {"num_splits": 1}),
     ("forced_splits_7", wl(L=(300, 700)), {"num_splits": 7}),
     # more than 64 sequences: every sequence takes S parts of a chunk sized from the longest

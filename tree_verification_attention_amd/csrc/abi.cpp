@@ -400,6 +400,25 @@ int tree_attn_forward(const ta_problem *p, void *o, float *lse, void *ws, size_t
     if (rc) return rc;
     if (p->B == 0) return TA_OK;
     if (!o || !lse) return TA_EINVAL;
+    if (p->dtype == TA_F32) {
+        const Plan pl = make_plan(p);
+        if (pl.n_splits == 1) {
+            // one split: the fp32 kernel takes the prefix and the tree keys of every row in one
+            // launch and writes the final output (the workspace is checked but not used)
+            if ((rc = check_prefix(p)) || (rc = check_tree(p))) return rc;
+            if (!ws_ok(pl, ws, ws_bytes)) return TA_EWORKSPACE;
+            AttnArgs a = make_args(p, pl, err_flag);
+            a.n_splits = 1;
+            a.with_prefix = 1;
+            a.with_tree = 1;
+            a.out_o = static_cast<float *>(o);
+            a.out_lse = lse;
+            a.part_so = 0;
+            a.part_sl = 0;
+            a.seq_parts = nullptr;
+            return status(ta::launch_attn_f32(a, stream));
+        }
+    }
     if ((rc = tree_attn_partials(p, ws, ws_bytes, err_flag, stream))) return rc;
     return tree_attn_combine(p, ws, ws_bytes, o, lse, stream);
 }
