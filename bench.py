@@ -208,7 +208,9 @@ def time_case(case, steps, warmup, label):
 def time_evicted(case, steps, warmup, label):
     """The fused forward and the split step of ``case``, each call timed with HIP events after a
     512 MiB evicting read (every step starts from cold caches, as a layer of a decode step whose
-    KV was last touched one step earlier)."""
+    KV was last touched one step earlier). The two calls alternate, so that both meet the same
+    state of the part's power management (a loop of one after a loop of the other would time
+    the first in the clock dip that follows the warm-up)."""
     import torch
 
     L = Launch(case)
@@ -216,12 +218,22 @@ def time_evicted(case, steps, warmup, label):
     print(f"[bench] {label}: warmup {warmup}", file=sys.stderr, flush=True)
     for _ in range(warmup):
         L.fwd()
-    torch.cuda.synchronize()
-    fwd_us = events_around(L.fwd, L.stream, steps, evict)
-    for _ in range(warmup):
         L.part()
     torch.cuda.synchronize()
-    part_us = events_around(L.part, L.stream, steps, evict)
+    evs = []
+    for _ in range(steps):
+        pair = []
+        for fn in (L.fwd, L.part):
+            evict()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(L.stream)
+            fn()
+            e1.record(L.stream)
+            pair.append((e0, e1))
+        evs.append(pair)
+    torch.cuda.synchronize()
+    fwd_us = [a.elapsed_time(b) * 1e3 for (a, b), _ in evs]
+    part_us = [a.elapsed_time(b) * 1e3 for _, (a, b) in evs]
     L.check_flag()
     return {"fwd_us": fwd_us, "part_us": part_us, "n_splits": L.n_splits}
 
