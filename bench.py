@@ -546,6 +546,8 @@ def time_next_rows(steps, warmup, seed):
         "kv_commit": {
             "workload": f"B={B}, Hkv=8, D=128 bf16, contiguous cache, {int(n.sum())} rows committed",
             "us": round(com_us, 2), "algorithmic_bytes": com_bytes,
+            "achieved_gbs": round(com_bytes / (com_us * 1e-6) / 1e9, 1), "peak_gbs": HBM_PEAK_GBS,
+            "frac": round(com_bytes / (com_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5),
             "note": "latency-bound: a few hundred KB move per call"},
     }
 
