@@ -141,6 +141,11 @@ SMALL = [
      {}),
     ("f32_forced_splits_3", wl(B=2, Hq=4, Hkv=2, D=128, T=16, dtype="f32", L=(0, 500)),
      {"num_splits": 3}),
+    # a last row block of at most 128 packed rows (half its wavefronts idle or fewer), with
+    # several parts per sequence dealt by length
+    ("short_last_block_g5_t128", wl(B=3, Hq=10, Hkv=2, T=128, L=(300, 2000), depth_cap=12), {}),
+    ("short_last_block_g5_t110", wl(B=2, Hq=10, Hkv=2, T=110, L=(700, 3000), depth_cap=12), {}),
+    ("short_last_block_d64_t80", wl(B=1, Hq=16, Hkv=4, D=64, T=80, L=(2000, 2000)), {}),
     ("forced_splits_1", wl(L=(300, 700)), {"num_splits": 1}),
     ("forced_splits_7", wl(L=(300, 700)), {"num_splits": 7}),
     # more than 64 sequences: every sequence takes S parts of a chunk sized from the longest
@@ -313,13 +318,17 @@ def test_device_errors_set_the_flag():
     assert err & _lib.TA_DEV_BAD_PARENT and err & _lib.TA_DEV_BAD_LEN
 
 
-@pytest.mark.parametrize("splits", [1, 2, 0])
-def test_rising_logits_take_the_exact_path(splits):
+@pytest.mark.parametrize("splits,shape", [(1, "g4"), (2, "g4"), (0, "g4"), (0, "g5_rowblocks")])
+def test_rising_logits_take_the_exact_path(splits, shape):
     """Prefix keys from position 256 on are shifted by +48 in every channel, so a row whose query
     sums to more than about one standard deviation scores them ~48 nats above the first tile: their
     exponentials against the first tile's maximum overflow fp32, and only the exact (moving
-    maximum) path gives a finite, correct result."""
-    w = wl(B=2, Hq=8, Hkv=2, T=16, L=(600, 900))
+    maximum) path gives a finite, correct result. "g5_rowblocks": 350 packed rows per KV head in
+    two row blocks of 8 wavefronts, the second with 94 rows."""
+    if shape == "g4":
+        w = wl(B=2, Hq=8, Hkv=2, T=16, L=(600, 900))
+    else:
+        w = wl(B=2, Hq=10, Hkv=2, T=70, L=(1500, 2500), depth_cap=12)
     case = inputs.make_case(w, 7)
     k = inputs.bf16_bits_to_f32(case.k_cache)
     for b, L in enumerate(case.seq_lens):
