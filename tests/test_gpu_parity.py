@@ -353,8 +353,8 @@ def test_determinism():
 # full configuration sizes, in the default launch plan (the one bench.py times)
 #
 # Every output row is compared for the headline layer (every prefix 64k), the drawn-length GQA
-# layer (contiguous and paged), the long-reasoning layer, the MHA layer and the sweep's small
-# trees. The larger sweep trees and the beam tree are compared on at least two rows of every
+# layer, the long-reasoning layer and the MHA layer (each contiguous and paged) and the sweep's
+# small trees. The larger sweep trees and the beam tree are compared on at least two rows of every
 # 32-row wavefront tile of every (sequence, KV head, row block). The oracle runs on every core this
 # process may use; its results are kept for the module, so the layouts and the unfused calls of
 # one workload share them.
@@ -434,7 +434,7 @@ def test_forward_full_size_every_row(name):
     compare_rows(case, o, lse, None, oracle_ref(name), f"full {name}")
 
 
-@pytest.mark.parametrize("name", ["gqa_64k", "gqa_64k_pinned"])
+@pytest.mark.parametrize("name", ["gqa_64k", "gqa_64k_pinned", "long_reasoning", "mha_7b"])
 def test_forward_full_size_paged_every_row(name):
     """The same layers with their prefixes in a pool of 64-key pages in random order."""
     case = full_case(name, "paged")
