@@ -349,6 +349,19 @@ def test_determinism():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_workspace_contents_do_not_matter(dtype):
+    """A workspace full of 0xFF bytes (NaN partials, part counts of -1) gives the same bits as a
+    fresh one: every slot the combine reads is written by the same call first."""
+    w = wl(L=(900, 1500)) if dtype == "bf16" else wl(D=64, T=9, dtype="f32", L=(1, 300))
+    case = inputs.make_case(w, 6)
+    o1, l1, _ = run_forward(case, num_splits=3)
+    dirty = torch.full((64 << 20,), 255, dtype=torch.uint8, device="cuda")
+    o2, l2, err = run_forward(case, num_splits=3, workspace=dirty)
+    assert err == 0
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 # ------------------------------------------------------------------------------------------------
 # full configuration sizes, in the default launch plan (the one bench.py times)
 #
