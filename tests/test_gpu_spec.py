@@ -95,6 +95,25 @@ def test_spec_sample_forced_trials():
     check(case, "always accept")
 
 
+@pytest.mark.parametrize("fill", [0, 255])
+def test_spec_sample_workspace_contents_do_not_matter(fill):
+    """Pass slots read as already written (0x00: sums of 0.0) or as NaN (0xFF) must not leak into
+    a call: the mass kernel resets every slot before the walk polls it."""
+    case = inputs.make_spec_case(3, 48, 30000, 2, tree="star", noise=0.7)
+    case.u_accept[:] = 0.97   # several trials per position: the walk's row passes
+    B, T1, V = case.p.shape
+    ws = torch.full((_lib.spec_sample_workspace_size(B, T1 - 1, V),), fill, dtype=torch.uint8,
+                    device="cuda")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out = _lib.spec_sample(dev(case.p), dev(case.q), dev(case.draft), dev(case.parent),
+                           dev(case.u_accept), dev(case.u_sample), ws=ws)
+    torch.cuda.synchronize()
+    n, path, nxt = [o.cpu().numpy() for o in out]
+    rn, rpath, rnxt = A.spec_sample(case.p, case.q, case.draft, case.parent, case.u_accept,
+                                    case.u_sample)
+    assert np.array_equal(n, rn) and np.array_equal(path, rpath) and np.array_equal(nxt, rnxt)
+
+
 def test_spec_sample_zero_residual_mass_accepts():
     case = inputs.make_spec_case(2, 6, 1000, 1, tree="chain")
     case.q[:] = case.p * np.float32(1.5)    # p <= q everywhere: no rejection is possible
