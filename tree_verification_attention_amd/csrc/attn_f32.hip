@@ -43,40 +43,6 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
     if (a.seq_parts && a.with_prefix && row == 0 && part == 0)
         for (int i = tid; i < a.B; i += kF32Threads) a.seq_parts[i] = a.n_splits;
 
-    // the query row and the tree's parents into LDS (all loads issued together)
-    const float *q = reinterpret_cast<const float *>(a.q) + b * a.q_sb + node * a.q_st + h * a.q_sh;
-    if (tid < D) qs[tid] = q[tid];
-    if (has_tree && tid < a.T) par[tid] = a.parent[(int64_t)b * a.T + tid];
-    for (int w = tid; w < TA_MAX_TREE / 32; w += kF32Threads) anc[w] = 0u;
-
-    // prefix keys [pb, pe) of this part
-    int pb = 0, pe = 0;
-    if (a.with_prefix) {
-        int L = a.seq_lens[b];
-        if (L < 0 || L > a.capacity) {
-            if (a.err && tid == 0) atomicOr(a.err, (int32_t)TA_DEV_BAD_LEN);
-            L = L < 0 ? 0 : a.capacity;
-        }
-        pb = part * a.chunk;
-        pe = min(pb + a.chunk, L);
-        if (pe < pb) pe = pb;
-    }
-    __syncthreads();
-    // ancestor-or-self bitmap of `node`, walked upwards in LDS by one thread while the others
-    // start on the prefix keys (it is read only after the barrier below)
-    if (has_tree && tid == 0) {
-        int j = node;
-        while (j >= 0) {
-            anc[j >> 5] |= 1u << (j & 31);
-            const int p = par[j];
-            if (p < -1 || p >= j) {
-                if (a.err) atomicOr(a.err, (int32_t)TA_DEV_BAD_PARENT);
-                break;
-            }
-            j = p;
-        }
-    }
-
     // every key slot keeps an online softmax over its keys; the four lanes of a slot hold DL
     // entries each of the dot product (summed by two butterfly steps) and of the output
     float m = -INFINITY, l = 0.f, acc[DL];
@@ -126,9 +92,73 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
             acc[4 * i + 3] = fmaf(pw, v4[i].w, acc[4 * i + 3]);
         }
     };
+    // The query row and the tree's parents go to LDS, and the length, the slot's first batch of
+    // prefix keys (contiguous layout) and, at D = 64, its first tree key to registers, all issued
+    // together:
+    // none of these addresses depends on the length or on the tree. Prefix keys past the length
+    // (cache rows below the capacity) and tree keys outside the node's ancestors are loaded and
+    // then dropped.
+    const float *q = reinterpret_cast<const float *>(a.q) + b * a.q_sb + node * a.q_st + h * a.q_sh;
+    if (tid < D) qs[tid] = q[tid];
+    if (has_tree && tid < a.T) par[tid] = a.parent[(int64_t)b * a.T + tid];
+    for (int w = tid; w < TA_MAX_TREE / 32; w += kF32Threads) anc[w] = 0u;
+    int L = a.with_prefix ? a.seq_lens[b] : 0;
+    const int pb = a.with_prefix ? part * a.chunk : 0;
+    const bool early = a.with_prefix && !a.block_table;
+    KeyVals kv0[KB];
+    bool got0[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+        const int k = slot + i * kKeySlots, j = pb + k;
+        got0[i] = early && k < a.chunk && j < a.capacity;
+        if (got0[i]) {
+            const int64_t off = b * a.kv_s0 + j * a.kv_s1 + g * a.kv_s2;
+            load_key(reinterpret_cast<const float *>(a.kc) + off,
+                     reinterpret_cast<const float *>(a.vc) + off, kv0[i]);
+        }
+    }
+    KeyVals tk;
+    const bool tgot = D == 64 && has_tree && slot < a.T;  // D = 128: registers for one batch only
+    if (tgot) {
+        const int64_t off = b * a.kt_sb + slot * a.kt_st + g * a.kt_sh;
+        load_key(reinterpret_cast<const float *>(a.kt) + off, reinterpret_cast<const float *>(a.vt) + off, tk);
+    }
+
+    // prefix keys [pb, pe) of this part
+    int pe = pb;
+    if (a.with_prefix) {
+        if (L < 0 || L > a.capacity) {
+            if (a.err && tid == 0) atomicOr(a.err, (int32_t)TA_DEV_BAD_LEN);
+            L = L < 0 ? 0 : a.capacity;
+        }
+        pe = max(pb, min(pb + a.chunk, L));
+    }
+    __syncthreads();
+    // ancestor-or-self bitmap of `node`, walked upwards in LDS by one thread while the others
+    // start on the prefix keys (it is read only after the barrier below)
+    if (has_tree && tid == 0) {
+        int j = node;
+        while (j >= 0) {
+            anc[j >> 5] |= 1u << (j & 31);
+            const int p = par[j];
+            if (p < -1 || p >= j) {
+                if (a.err) atomicOr(a.err, (int32_t)TA_DEV_BAD_PARENT);
+                break;
+            }
+            j = p;
+        }
+    }
+
     // prefix keys (a slot's four lanes agree on every key, so the branches stay uniform per
     // slot; the butterfly stays inside the slot's lanes)
-    for (int k0 = slot; k0 < pe - pb; k0 += KB * kKeySlots) {
+    int k_first = slot;
+    if (early) {  // the batch loaded with the query
+#pragma unroll
+        for (int i = 0; i < KB; ++i)
+            if (got0[i] && slot + i * kKeySlots < pe - pb) take_key(kv0[i]);
+        k_first = slot + KB * kKeySlots;
+    }
+    for (int k0 = k_first; k0 < pe - pb; k0 += KB * kKeySlots) {
         KeyVals kv[KB];
         bool ok[KB];
 #pragma unroll
@@ -164,6 +194,10 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
                 const int j = j0 + i * kKeySlots;
                 ok[i] = j < a.T && ((anc[j >> 5] >> (j & 31)) & 1u);
                 if (!ok[i]) continue;
+                if (tgot && j == slot) {  // loaded with the query
+                    kv[i] = tk;
+                    continue;
+                }
                 const int64_t off = b * a.kt_sb + j * a.kt_st + g * a.kt_sh;
                 load_key(reinterpret_cast<const float *>(a.kt) + off, reinterpret_cast<const float *>(a.vt) + off, kv[i]);
             }
