@@ -263,3 +263,24 @@ def test_gdn_calls_reject_bad_arguments_on_the_host(lib):
     assert verify(B=0) == _lib.TA_OK
     assert lib.tree_gdn_commit(FAKE, FAKE, FAKE, FAKE, 2, 16, 2, 4, 64, 64, FAKE, FAKE, 0,
                                None, None) == _lib.TA_EINVAL
+
+
+@pytest.mark.parametrize("compiler,std", [("gcc", "-std=c11"), ("g++", "-std=c++17")])
+def test_header_compiles_as_c_and_cxx(tmp_path, compiler, std):
+    """The public header is plain C: it compiles on its own as C11 and as C++17 (the HIP
+    runtime API header supplies hipStream_t), with every declaration usable from C."""
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not available")
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "treeattn.h"\n'
+                   "int use(const ta_problem *p, size_t *n) {\n"
+                   "    int k = 0;\n"
+                   "    return tree_attn_workspace_size(p, n) | tree_attn_num_splits(p, &k);\n"
+                   "}\n")
+    lang = ["-x", "c++"] if compiler == "g++" else []
+    cmd = [compiler, std, "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include",
+           "-I/opt/rocm/include", *lang, "-c", str(src), "-o", str(tmp_path / "use_header.o")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
