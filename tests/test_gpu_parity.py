@@ -146,6 +146,12 @@ SMALL = [
     ("short_last_block_g5_t128", wl(B=3, Hq=10, Hkv=2, T=128, L=(300, 2000), depth_cap=12), {}),
     ("short_last_block_g5_t110", wl(B=2, Hq=10, Hkv=2, T=110, L=(700, 3000), depth_cap=12), {}),
     ("short_last_block_d64_t80", wl(B=1, Hq=16, Hkv=4, D=64, T=80, L=(2000, 2000)), {}),
+    # exactly 64 sequences, the most whose parts are still dealt by length
+    ("batch64_dealt", wl(B=64, Hq=4, Hkv=2, T=4, L=(0, 700)), {}),
+    # 256 nodes x 4 query heads: four 256-row blocks per KV head
+    ("t256_g4_four_rowblocks", wl(B=1, Hq=8, Hkv=2, T=256, L=(500, 1000), depth_cap=16), {}),
+    # every prefix a multiple of 64 keys: no tail tile in the masked part
+    ("lengths_multiple_of_64", wl(B=3, L=(640, 640)), {}),
     ("forced_splits_1", wl(L=(300, 700)), {"num_splits": 1}),
     ("forced_splits_7", wl(L=(300, 700)), {"num_splits": 7}),
     # more than 64 sequences: every sequence takes S parts of a chunk sized from the longest
